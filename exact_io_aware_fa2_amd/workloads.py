@@ -1,0 +1,107 @@
+"""Seeded synthetic inputs for the attention workloads (no attention arithmetic here).
+
+This module only draws random tensors and names the workload shapes.  It is the one
+module that both the HIP path's tests/bench and the float64 oracle's callers share;
+it holds none of the method's arithmetic.
+
+Draw recipe (fixed order q, k, v, dO): ``torch.randn(shape, float32) * sigma`` from a
+CPU ``torch.Generator`` seeded with ``seed``, then a round-to-nearest-even cast to the
+compute dtype.  Tensors are [batch, seqlen, heads, headdim] (the layout of the usage
+example on bmjup.com "FlashAttention-2 ... 实战解析", section 4).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str          # "fp32" or "bf16"
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    window: int = 0
+    sigma_q: float = 1.0
+    sigma_k: float = 1.0
+    sigma_v: float = 1.0
+    sigma_do: float = 1.0
+    backward: bool = True
+    seed: int = 1000
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) rounded to float32 (the value handed to the kernels)."""
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+    def replace(self, **kw) -> "Workload":
+        from dataclasses import replace
+        return replace(self, **kw)
+
+
+# The five configurations the method is measured on (the fifth runs twice: causal, and
+# causal with a 4096-key sliding window on the same tensors).
+WORKLOADS = {
+    "fp32_b1_h2_n256_d64": Workload("fp32_b1_h2_n256_d64", "fp32", 1, 2, 2, 256, 64, False,
+                                    backward=False, seed=1001),
+    "bf16_b2_h16_n2048_d128_causal_sigma4": Workload(
+        "bf16_b2_h16_n2048_d128_causal_sigma4", "bf16", 2, 16, 16, 2048, 128, True,
+        sigma_q=4.0, sigma_k=4.0, seed=1002),
+    "bf16_b2_h32_n8192_d128_causal": Workload("bf16_b2_h32_n8192_d128_causal", "bf16",
+                                              2, 32, 32, 8192, 128, True, seed=1003),
+    "bf16_b1_h16_n16384_d256": Workload("bf16_b1_h16_n16384_d256", "bf16", 1, 16, 16, 16384,
+                                        256, False, seed=1004),
+    "bf16_b1_hq32_hkv8_n65536_d128_causal": Workload(
+        "bf16_b1_hq32_hkv8_n65536_d128_causal", "bf16", 1, 32, 8, 65536, 128, True, seed=1005),
+    "bf16_b1_hq32_hkv8_n65536_d128_causal_window4096": Workload(
+        "bf16_b1_hq32_hkv8_n65536_d128_causal_window4096", "bf16", 1, 32, 8, 65536, 128, True,
+        window=4096, seed=1005),
+}
+
+HEADLINE = "bf16_b2_h32_n8192_d128_causal"
+
+_TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+
+def torch_dtype(w: Workload) -> torch.dtype:
+    return _TORCH_DTYPE[w.dtype]
+
+
+def make_inputs(w: Workload, device: str | torch.device = "cpu", with_grad: bool | None = None):
+    """Draw (q, k, v, dO) for workload ``w``; dO is None for forward-only workloads.
+
+    The draw happens on the CPU in float32 so the values do not depend on the device;
+    the rounded tensors are then moved to ``device``.
+    """
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    dt = torch_dtype(w)
+    shp_q = (w.B, w.N, w.Hq, w.d)
+    shp_kv = (w.B, w.N, w.Hkv, w.d)
+
+    def draw(shape, sigma):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        return x.to(dt).to(device)
+
+    q = draw(shp_q, w.sigma_q)
+    k = draw(shp_kv, w.sigma_k)
+    v = draw(shp_kv, w.sigma_v)
+    want_grad = w.backward if with_grad is None else with_grad
+    do = draw(shp_q, w.sigma_do) if want_grad else None
+    return q, k, v, do
+
+
+def small_case(name: str, dtype: str, B: int, Hq: int, Hkv: int, N: int, d: int, causal: bool,
+               window: int = 0, seed: int = 7, sigma_qk: float = 1.0) -> Workload:
+    """A parity-test workload of arbitrary (small) shape."""
+    return Workload(name, dtype, B, Hq, Hkv, N, d, causal, window, sigma_qk, sigma_qk,
+                    seed=seed)

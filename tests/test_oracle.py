@@ -1,0 +1,398 @@
+"""Pins for the float64 oracle (CPU only; no GPU, no HIP library).
+
+Every test checks the oracle against something other than itself: hand-derived
+closed forms, invariants of the softmax, central finite differences, brute-force
+enumeration, or an independent library routine (PyTorch's CPU float64 attention).
+"""
+
+import ast
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import (attention_probs, attn_bwd, attn_bwd_dkdv_cols, attn_bwd_dq_rows,
+                    attn_bwd_head, attn_fwd, attn_fwd_head, attn_fwd_rows, allowed_keys,
+                    attended_pairs)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+# ------------------------------------------------------------------ helpers
+def _eval_expr(s: str) -> float:
+    """Evaluate a fixture expression: numbers, + - * /, unary minus and ln()."""
+    def ev(node):
+        if isinstance(node, ast.Expression):
+            return ev(node.body)
+        if isinstance(node, ast.Constant) and isinstance(node.value, (int, float)):
+            return float(node.value)
+        if isinstance(node, ast.UnaryOp) and isinstance(node.op, ast.USub):
+            return -ev(node.operand)
+        if isinstance(node, ast.BinOp):
+            a, b = ev(node.left), ev(node.right)
+            if isinstance(node.op, ast.Add):
+                return a + b
+            if isinstance(node.op, ast.Sub):
+                return a - b
+            if isinstance(node.op, ast.Mult):
+                return a * b
+            if isinstance(node.op, ast.Div):
+                return a / b
+        if (isinstance(node, ast.Call) and isinstance(node.func, ast.Name)
+                and node.func.id == "ln" and len(node.args) == 1):
+            return math.log(ev(node.args[0]))
+        raise ValueError(f"unsupported expression {s!r}")
+    return ev(ast.parse(s, mode="eval"))
+
+
+def _arr(x):
+    return np.vectorize(_eval_expr, otypes=[float])(np.array(x, dtype=object))
+
+
+def _rand(rng, *shape, sigma=1.0):
+    return rng.standard_normal(shape) * sigma
+
+
+# ------------------------------------------------------------------ golden fixtures
+def _golden_cases():
+    with open(GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_hand_worked_fixture(case):
+    q = _arr(case["q"])[None]
+    k = _arr(case["k"])[None]
+    v = _arr(case["v"])[None]
+    scale = _eval_expr(case["scale"])
+    o, lse = attn_fwd(q, k, v, case["causal"], case["window"], scale)
+    np.testing.assert_allclose(o[0], _arr(case["O"]), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0], _arr(case["LSE"]), rtol=0, atol=1e-13)
+    if "dO" in case:
+        do = _arr(case["dO"])[None]
+        dq, dk, dv, _ = attn_bwd(q, k, v, do, case["causal"], case["window"], scale)
+        np.testing.assert_allclose(dq[0], _arr(case["dQ"]), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dk[0], _arr(case["dK"]), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dv[0], _arr(case["dV"]), rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------ masks
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("window", [0, 1, 3, 7])
+def test_allowed_keys_enumeration(causal, window):
+    n = 11
+    for i in range(n):
+        lo, hi = allowed_keys(i, n, causal, window)
+        brute = [j for j in range(n)
+                 if (not causal or j <= i) and (window == 0 or j >= i - window + 1)]
+        assert list(range(lo, hi)) == brute
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 5), (False, 5), (True, 1)])
+def test_attended_pairs_closed_form(causal, window):
+    n = 37
+    if not causal and window == 0:
+        expect = n * n
+    elif causal and window == 0:
+        expect = n * (n + 1) // 2
+    elif causal:
+        w = window
+        expect = w * (w + 1) // 2 + (n - w) * w
+    else:
+        # non-causal left bound: row i sees n - max(0, i - w + 1) keys
+        expect = sum(n - max(0, i - window + 1) for i in range(n))
+    assert attended_pairs(n, causal, window) == expect
+
+
+# ------------------------------------------------------------------ forward pins
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 4), (False, 4)])
+def test_rows_sum_to_one_and_masked_zero(causal, window):
+    rng = np.random.default_rng(0)
+    n, d = 23, 8
+    q, k = _rand(rng, n, d, sigma=3), _rand(rng, n, d, sigma=3)
+    p = attention_probs(q, k, causal, window, 0.4)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-14)
+    for i in range(n):
+        lo, hi = allowed_keys(i, n, causal, window)
+        assert np.all(p[i, :lo] == 0) and np.all(p[i, hi:] == 0)
+        assert np.all(p[i, lo:hi] > 0)
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 3)])
+def test_v_ones_gives_ones(causal, window):
+    rng = np.random.default_rng(1)
+    b, n, h, d = 2, 19, 2, 5
+    q, k = _rand(rng, b, n, h, d, sigma=4), _rand(rng, b, n, h, d, sigma=4)
+    v = np.ones((b, n, h, 7))
+    o, _ = attn_fwd(q, k, v, causal, window, 0.7)
+    np.testing.assert_allclose(o, 1.0, atol=1e-13)
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 4), (False, 4)])
+def test_equal_scores_give_mean_of_v(which, causal, window):
+    rng = np.random.default_rng(2)
+    n, d = 17, 6
+    q, k, v = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    if which == "q":
+        q[:] = 0
+    else:
+        k[:] = 0
+    o, lse = attn_fwd_head(q, k, v, causal, window, 1.3)
+    for i in range(n):
+        lo, hi = allowed_keys(i, n, causal, window)
+        np.testing.assert_allclose(o[i], v[lo:hi].mean(axis=0), atol=1e-13)
+        np.testing.assert_allclose(lse[i], math.log(hi - lo), atol=1e-13)
+
+
+def test_causal_row0_is_v0():
+    rng = np.random.default_rng(3)
+    n, d = 9, 4
+    q, k, v = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    o, lse = attn_fwd_head(q, k, v, True, 0, 0.5)
+    np.testing.assert_allclose(o[0], v[0], atol=1e-15)
+    np.testing.assert_allclose(lse[0], 0.5 * q[0] @ k[0], atol=1e-15)
+
+
+def test_two_keys_sigmoid_closed_form():
+    rng = np.random.default_rng(4)
+    q, k, v = _rand(rng, 2, 1), _rand(rng, 2, 1), _rand(rng, 2, 1)
+    scale = 0.9
+    o, lse = attn_fwd_head(q, k, v, False, 0, scale)
+    for i in range(2):
+        s0, s1 = scale * q[i, 0] * k[0, 0], scale * q[i, 0] * k[1, 0]
+        p0 = 1.0 / (1.0 + math.exp(-(s0 - s1)))
+        assert abs(o[i, 0] - (p0 * v[0, 0] + (1 - p0) * v[1, 0])) < 1e-14
+        assert abs(lse[i] - math.log(math.exp(s0) + math.exp(s1))) < 1e-14
+
+
+def test_large_logits_stay_finite():
+    # scores of several hundred: the plain exp would overflow without the max shift
+    q = np.array([[30.0, 0.0], [0.0, 30.0]])
+    k = np.array([[30.0, 0.0], [29.0, 0.0], [0.0, 30.0]])
+    v = np.array([[1.0], [2.0], [3.0]])
+    o, lse = attn_fwd_head(q, k, v, False, 0, 1.0)
+    # row 0: s = (900, 870, 0) -> weight of key 1 relative e^-30
+    e = math.exp(-30.0)
+    np.testing.assert_allclose(o[0, 0], (1 + 2 * e) / (1 + e), rtol=1e-14)
+    np.testing.assert_allclose(lse[0], 900 + math.log1p(e), rtol=1e-15)
+    np.testing.assert_allclose(o[1, 0], 3.0, rtol=1e-14)
+
+
+def test_shift_and_permutation_equivariance():
+    rng = np.random.default_rng(5)
+    n, d = 13, 4
+    q, k, v = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    s = 0.8
+    o, lse = attn_fwd_head(q, k, v, False, 0, s)
+    c = rng.standard_normal(d)
+    # v -> v + c shifts O by c (rows of P sum to one)
+    o2, _ = attn_fwd_head(q, k, v + c, False, 0, s)
+    np.testing.assert_allclose(o2, o + c, atol=1e-13)
+    # k -> k + c adds s*q_i.c to every score of row i: O unchanged, LSE shifted
+    o3, lse3 = attn_fwd_head(q, k + c, v, False, 0, s)
+    np.testing.assert_allclose(o3, o, atol=1e-13)
+    np.testing.assert_allclose(lse3, lse + s * q @ c, atol=1e-13)
+    # permuting (k, v) jointly leaves O unchanged (non-causal)
+    perm = rng.permutation(n)
+    o4, lse4 = attn_fwd_head(q, k[perm], v[perm], False, 0, s)
+    np.testing.assert_allclose(o4, o, atol=1e-13)
+    np.testing.assert_allclose(lse4, lse, atol=1e-13)
+    # permuting queries permutes O
+    o5, lse5 = attn_fwd_head(q[perm], k, v, False, 0, s)
+    np.testing.assert_allclose(o5, o[perm], atol=1e-13)
+    np.testing.assert_allclose(lse5, lse[perm], atol=1e-13)
+
+
+def test_scale_folds_into_q():
+    rng = np.random.default_rng(6)
+    n, d = 11, 3
+    q, k, v = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    o1, l1 = attn_fwd_head(q, k, v, True, 0, 0.25)
+    o2, l2 = attn_fwd_head(0.25 * q, k, v, True, 0, 1.0)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-14)
+    # a negative scale is the same as negating q
+    o3, l3 = attn_fwd_head(q, k, v, True, 3, -0.5)
+    o4, l4 = attn_fwd_head(-q, k, v, True, 3, 0.5)
+    np.testing.assert_allclose(o3, o4, atol=1e-14)
+    np.testing.assert_allclose(l3, l4, atol=1e-14)
+
+
+def test_window_at_least_n_equals_plain_causal():
+    rng = np.random.default_rng(7)
+    n, d = 15, 4
+    q, k, v = _rand(rng, n, d), _rand(rng, n, d), _rand(rng, n, d)
+    o1, l1 = attn_fwd_head(q, k, v, True, 0, 0.6)
+    o2, l2 = attn_fwd_head(q, k, v, True, n, 0.6)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    # window 1 with causal: each row sees only itself
+    o3, l3 = attn_fwd_head(q, k, v, True, 1, 0.6)
+    np.testing.assert_allclose(o3, v, atol=1e-15)
+    np.testing.assert_allclose(l3, 0.6 * np.einsum("nd,nd->n", q, k), atol=1e-14)
+
+
+def test_gqa_equals_repeated_kv_heads():
+    rng = np.random.default_rng(8)
+    b, n, hq, hkv, d = 2, 10, 6, 2, 3
+    q = _rand(rng, b, n, hq, d)
+    k, v = _rand(rng, b, n, hkv, d), _rand(rng, b, n, hkv, d)
+    o, lse = attn_fwd(q, k, v, True, 0, 0.5)
+    g = hq // hkv
+    for h in range(hq):
+        for bi in range(b):
+            oh, lh = attn_fwd_head(q[bi, :, h], k[bi, :, h // g], v[bi, :, h // g], True, 0, 0.5)
+            np.testing.assert_array_equal(o[bi, :, h], oh)
+            np.testing.assert_array_equal(lse[bi, h], lh)
+
+
+def test_row_chunking_is_exact():
+    rng = np.random.default_rng(9)
+    n, d = 300, 8
+    q, k, v, do = (_rand(rng, n, d) for _ in range(4))
+    for causal, window in [(True, 0), (True, 50), (False, 0), (False, 40)]:
+        o1, l1 = attn_fwd_head(q, k, v, causal, window, 0.4, row_chunk=64)
+        o2, l2 = attn_fwd_head(q, k, v, causal, window, 0.4, row_chunk=7)
+        np.testing.assert_allclose(o1, o2, atol=1e-12)
+        np.testing.assert_allclose(l1, l2, atol=1e-12)
+        g1 = attn_bwd_head(q, k, v, do, causal, window, 0.4, row_chunk=64)
+        g2 = attn_bwd_head(q, k, v, do, causal, window, 0.4, row_chunk=13)
+        for a, b_ in zip(g1, g2):
+            np.testing.assert_allclose(a, b_, atol=1e-12)
+
+
+def test_sampled_rows_match_full():
+    rng = np.random.default_rng(10)
+    n, d = 200, 8
+    q, k, v, do = (_rand(rng, n, d) for _ in range(4))
+    rows = np.array([0, 1, 63, 64, 127, 199])
+    cols = np.array([0, 5, 100, 150, 199])
+    for causal, window in [(True, 0), (True, 30), (False, 0)]:
+        o, l = attn_fwd_head(q, k, v, causal, window, 0.3)
+        orows, lrows = attn_fwd_rows(q, k, v, rows, causal, window, 0.3)
+        np.testing.assert_allclose(orows, o[rows], atol=1e-13)
+        np.testing.assert_allclose(lrows, l[rows], atol=1e-13)
+        dq, dk, dv, dvec = attn_bwd_head(q, k, v, do, causal, window, 0.3)
+        dqr, dr = attn_bwd_dq_rows(q, k, v, do, rows, causal, window, 0.3)
+        np.testing.assert_allclose(dqr, dq[rows], atol=1e-13)
+        np.testing.assert_allclose(dr, dvec[rows], atol=1e-13)
+        dkc, dvc = attn_bwd_dkdv_cols(q, k, v, do, cols, causal, window, 0.3, row_chunk=37)
+        np.testing.assert_allclose(dkc, dk[cols], atol=1e-12)
+        np.testing.assert_allclose(dvc, dv[cols], atol=1e-12)
+
+
+# ------------------------------------------------------------------ backward pins
+def _loss(q, k, v, do, causal, window, scale):
+    o, _ = attn_fwd(q, k, v, causal, window, scale)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 2), (False, 2)])
+def test_finite_differences(causal, window):
+    rng = np.random.default_rng(11)
+    b, n, hq, hkv, d = 1, 5, 2, 1, 3
+    q = _rand(rng, b, n, hq, d)
+    k = _rand(rng, b, n, hkv, d)
+    v = _rand(rng, b, n, hkv, d)
+    do = _rand(rng, b, n, hq, d)
+    scale = 0.7
+    dq, dk, dv, _ = attn_bwd(q, k, v, do, causal, window, scale)
+    h = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy()
+            xp[idx] += h
+            xm = x.copy()
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], do, causal, window, scale)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], do, causal, window, scale)
+            num[idx] = (lp - lm) / (2 * h)
+        err = np.abs(num - g).max() / max(1e-12, np.abs(g).max())
+        assert err < 1e-6, (name, err)
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 6)])
+def test_backward_invariants(causal, window):
+    rng = np.random.default_rng(12)
+    b, n, hq, hkv, d = 1, 29, 4, 2, 5
+    q, do = _rand(rng, b, n, hq, d), _rand(rng, b, n, hq, d)
+    k, v = _rand(rng, b, n, hkv, d), _rand(rng, b, n, hkv, d)
+    scale = 0.45
+    o, _ = attn_fwd(q, k, v, causal, window, scale)
+    dq, dk, dv, dvec = attn_bwd(q, k, v, do, causal, window, scale)
+    g = hq // hkv
+    # D_i equals dO_i . O_i (rows of P sum to one)
+    np.testing.assert_allclose(dvec, np.einsum("bnhd,bnhd->bhn", do, o), atol=1e-12)
+    # sum_j dK_j = 0 (invariance of softmax to a per-row shift of K)
+    np.testing.assert_allclose(dk.sum(axis=1), 0.0, atol=1e-12)
+    # sum_j dV_j = sum over the group's query heads of sum_i dO_i
+    for hk in range(hkv):
+        expect = do[:, :, hk * g:(hk + 1) * g].sum(axis=(1, 2))
+        np.testing.assert_allclose(dv[:, :, hk].sum(axis=1), expect, atol=1e-12)
+    # rows of dS sum to zero: checked through sum_j dS_ij k_j with k = const
+    kc = np.ones_like(k)
+    dq_c, _, _, _ = attn_bwd(q, kc, v, do, causal, window, scale)
+    np.testing.assert_allclose(dq_c, 0.0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ independent library
+@pytest.mark.parametrize("causal,window,hq,hkv", [(False, 0, 4, 4), (True, 0, 4, 2), (True, 16, 4, 1),
+                                                  (False, 16, 2, 2)])
+def test_matches_torch_sdpa_cpu_float64(causal, window, hq, hkv):
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(13)
+    b, n, d = 2, 70, 16
+    q = _rand(rng, b, n, hq, d, sigma=2)
+    k = _rand(rng, b, n, hkv, d, sigma=2)
+    v = _rand(rng, b, n, hkv, d)
+    do = _rand(rng, b, n, hq, d)
+    scale = 1 / math.sqrt(d)
+    o, lse = attn_fwd(q, k, v, causal, window, scale)
+    dq, dk, dv, _ = attn_bwd(q, k, v, do, causal, window, scale)
+
+    tq = torch.tensor(q).transpose(1, 2).requires_grad_()
+    tk = torch.tensor(k).transpose(1, 2).requires_grad_()
+    tv = torch.tensor(v).transpose(1, 2).requires_grad_()
+    g = hq // hkv
+    ke = tk.repeat_interleave(g, dim=1)
+    ve = tv.repeat_interleave(g, dim=1)
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    mask = torch.ones(n, n, dtype=torch.bool)
+    if causal:
+        mask &= j <= i
+    if window:
+        mask &= j >= i - window + 1
+    to = F.scaled_dot_product_attention(tq, ke, ve, attn_mask=mask, scale=scale)
+    to.backward(torch.tensor(do).transpose(1, 2))
+    np.testing.assert_allclose(o, to.detach().transpose(1, 2).numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.transpose(1, 2).numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.transpose(1, 2).numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.transpose(1, 2).numpy(), rtol=0, atol=1e-11)
+    # LSE against torch.logsumexp of the masked score matrix
+    s = torch.einsum("bhnd,bhmd->bhnm", tq.detach(), ke.detach()) * scale
+    s = s.masked_fill(~mask, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_process_pool_matches_serial():
+    rng = np.random.default_rng(14)
+    b, n, hq, hkv, d = 1, 40, 4, 2, 8
+    q, do = _rand(rng, b, n, hq, d), _rand(rng, b, n, hq, d)
+    k, v = _rand(rng, b, n, hkv, d), _rand(rng, b, n, hkv, d)
+    o1, l1 = attn_fwd(q, k, v, True, 0, 0.3)
+    o2, l2 = attn_fwd(q, k, v, True, 0, 0.3, workers=2)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    g1 = attn_bwd(q, k, v, do, True, 0, 0.3)
+    g2 = attn_bwd(q, k, v, do, True, 0, 0.3, workers=2)
+    for a, b_ in zip(g1, g2):
+        np.testing.assert_allclose(a, b_, atol=1e-14)
