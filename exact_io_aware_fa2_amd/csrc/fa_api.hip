@@ -1,0 +1,125 @@
+// fa_api.hip -- the extern "C" boundary of libfa.so (declared in include/fa.h).
+//
+// Every entry point validates its arguments on the host before enqueuing anything, never
+// allocates or synchronises, and reports failures through a status code plus a
+// thread-local message.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/fa.h"
+#include "fa_kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fa_status fail(fa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+fa_status fail(fa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+fa_status ok() {
+  g_err[0] = '\0';
+  return FA_OK;
+}
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;  // kernels index rows with 32-bit ints
+
+fa_status check_common(const char* fn, int B, int Hq, int Hkv, int N, int d, int causal,
+                       int window, float scale) {
+  (void)causal;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0 || d <= 0)
+    return fail(FA_ERR_INVALID_ARG, "%s: sizes must be positive (B=%d Hq=%d Hkv=%d N=%d d=%d)",
+                fn, B, Hq, Hkv, N, d);
+  if (Hq % Hkv != 0)
+    return fail(FA_ERR_INVALID_ARG, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (window < 0) return fail(FA_ERR_INVALID_ARG, "%s: window=%d must be >= 0", fn, window);
+  if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
+  if (d != 64 && d != 128 && d != 256)
+    return fail(FA_ERR_UNSUPPORTED, "%s: head dim %d not supported (64, 128 or 256)", fn, d);
+  const int64_t rows = (int64_t)B * N * Hq;
+  if (rows * d >= kMaxElems || (int64_t)B * Hq * N >= kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "%s: B*N*Hq*d = %lld elements exceeds 2^31", fn,
+                (long long)(rows * d));
+  return FA_OK;
+}
+
+fa_status launched(const char* fn, hipError_t e) {
+  if (e != hipSuccess)
+    return fail(FA_ERR_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                 void* stream) {
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "fa_fwd: null pointer");
+  fa_status st = check_common("fa_fwd", B, Hq, Hkv, N, d, causal, window, scale);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal ? 1 : 0, window,
+                fabsf(scale) * fa::kHostLog2e, scale * fa::kHostLog2e, scale < 0.f ? 1 : 0};
+  return launched("fa_fwd", fa::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
+                      int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                      float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp32: null pointer");
+  fa_status st = check_common("fa_fwd_fp32", B, Hq, Hkv, N, d, causal, window, scale);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal ? 1 : 0, window,
+                fabsf(scale) * fa::kHostLog2e, scale * fa::kHostLog2e, 0};
+  return launched("fa_fwd_fp32", fa::launch_fwd_fp32(a, (hipStream_t)stream));
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int window) {
+  if (check_common("fa_bwd_workspace_size", B, Hq, Hkv, N, d, causal, window, 1.f) != FA_OK)
+    return 0;
+  const size_t dvec = align256((size_t)B * Hq * N * sizeof(float));
+  const size_t dqacc = (size_t)B * N * Hq * d * sizeof(float);
+  return dvec + dqacc;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+                 int N, int d, int causal, int window, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd: null pointer");
+  fa_status st = check_common("fa_bwd", B, Hq, Hkv, N, d, causal, window, scale);
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_workspace_size(B, Hq, Hkv, N, d, causal, window);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "fa_bwd: workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(FA_ERR_WORKSPACE, "fa_bwd: workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  float* dvec = reinterpret_cast<float*>(ws);
+  float* dq_acc = reinterpret_cast<float*>(ws + align256((size_t)B * Hq * N * sizeof(float)));
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dvec, dq_acc, B, Hq, Hkv, N, d,
+                causal ? 1 : 0, window, scale, scale * fa::kHostLog2e};
+  return launched("fa_bwd", fa::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+const char* fa_last_error(void) { return g_err; }
+
+const char* fa_version(void) { return "libfa 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// fa_common.hpp -- device helpers shared by the gfx950 attention kernels.
+//
+// Matrix-core conventions (v_mfma_f32_32x32x16_bf16, wave64), checked on gfx950:
+//   A operand (32 x 16, M x K): lane l holds A[l % 32][8 * (l / 32) + i], i = 0..7
+//   B operand (16 x 32, K x N): lane l holds B[8 * (l / 32) + i][l % 32]
+//   C/D (32 x 32 fp32):         lane l, element r holds
+//                               C[(r / 4) * 8 + (l / 32) * 4 + (r % 4)][l % 32]
+// Because the reduction index only has to agree between A and B, an accumulator C[m][n]
+// can feed a later product directly as a B operand B[k = m][n] (the kernels pick the
+// matching key/row order for the other operand).
+//
+// ds_read_b64_tr_b16 (gfx950): inside each group of 16 lanes, the four rows loaded by
+// lanes 4r..4r+3 (four 16-bit values each) form a 4 x 16 block; lane j receives column j
+// of it.  This turns a row-major [key][d] tile in LDS into the per-lane "8 keys at one d"
+// operand that a product contracting over keys needs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef uint16_t bf16_t;  // storage type of a bfloat16 in global memory
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Two transposed 64-bit LDS reads -> one 8 x bf16 operand (elements 0..3 from p0,
+// 4..7 from p1).  Pointers are generic pointers into __shared__ memory.
+__device__ __forceinline__ bf16x8 lds_read_tr_x2(const void* p0, const void* p1) {
+  i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  bf16x8 r;
+  bf16x4 ab = __builtin_bit_cast(bf16x4, a);
+  bf16x4 bb = __builtin_bit_cast(bf16x4, b);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[i] = ab[i];
+    r[4 + i] = bb[i];
+  }
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const void* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ uint4 gload16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// Flip the sign bit of 8 packed bfloat16 values (exact negation).
+__device__ __forceinline__ bf16x8 negate8(const bf16x8& x) {
+  uint4 u = __builtin_bit_cast(uint4, x);
+  u.x ^= 0x80008000u;
+  u.y ^= 0x80008000u;
+  u.z ^= 0x80008000u;
+  u.w ^= 0x80008000u;
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Round-to-nearest-even float -> bfloat16 (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return r;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max / sum across the two 32-lane halves of a wave (lane l <-> lane l ^ 32).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).  Map the
+// hardware block id so that consecutive logical ids land on the same XCD: XCD x runs the
+// logical ids [x * T / 8, (x + 1) * T / 8) in order.  A bijection for any T.
+__device__ __forceinline__ int xcd_remap(int hw, int total) {
+  constexpr int kXcd = 8;
+  const int per = total / kXcd, rem = total % kXcd;
+  const int xcd = hw % kXcd, slot = hw / kXcd;
+  if (per == 0) return hw;
+  // XCDs [0, rem) receive per + 1 blocks, the others per blocks.
+  if (slot >= per + (xcd < rem ? 1 : 0)) return hw;  // unreachable for a full grid
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+}  // namespace fa

@@ -1,0 +1,45 @@
+// fa_kernels.hpp -- host-side launch interface between the C ABI (fa_api.hip) and the
+// kernel files.  Arguments are validated by the caller before any launcher runs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+constexpr float kHostLog2e = 1.4426950408889634f;
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N, d, causal, window;
+  float c_log2;         // |scale| * log2(e)
+  float c_log2_signed;  // scale * log2(e)
+  int neg_q;            // 1 when scale < 0 (Q is negated exactly inside the kernel)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;    // D = rowsum(dO * O), [B, Hq, N]
+  float* dq_acc;  // float32 dQ accumulator, [B, N, Hq, d]
+  int B, Hq, Hkv, N, d, causal, window;
+  float scale;
+  float c_log2_signed;  // scale * log2(e)
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t st);
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
+
+}  // namespace fa

@@ -1,0 +1,169 @@
+"""Thin ctypes binding of libfa.so (argument marshalling only).
+
+The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_bwd``, ``fa_bwd_workspace_size``,
+``fa_last_error`` and ``fa_version`` mirror the C entry points of ``include/fa.h`` one to
+one; they take torch tensors only as carriers of device pointers and of the current HIP
+stream.  ``forward`` / ``backward`` add output allocation for convenience.  Every step of
+the computation runs in the HIP kernels of libfa.so: when the library is missing, loading
+raises instead of falling back to anything else.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+_lib = None
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_bwd_workspace_size", "fa_last_error",
+            "fa_version")
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libfa status {status}: {message}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m exact_io_aware_fa2_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_fp32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp32.restype = i
+    lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_bwd_workspace_size.restype = sz
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_bwd.restype = i
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FaError(status, fa_last_error())
+
+
+# ------------------------------------------------------------ 1:1 C entry points
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, stream=None) -> int:
+    return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                         int(causal), int(window), float(scale), _stream(stream))
+
+
+def fa_fwd_fp32(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, stream=None) -> int:
+    return load().fa_fwd_fp32(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                              int(causal), int(window), float(scale), _stream(stream))
+
+
+def fa_bwd_workspace_size(B, Hq, Hkv, N, d, causal, window) -> int:
+    return load().fa_bwd_workspace_size(B, Hq, Hkv, N, d, int(causal), int(window))
+
+
+def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
+           workspace, workspace_bytes, stream=None) -> int:
+    return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq),
+                         _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal), int(window),
+                         float(scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_last_error() -> str:
+    return load().fa_last_error().decode()
+
+
+def fa_version() -> str:
+    return load().fa_version().decode()
+
+
+# ------------------------------------------------------------ tensor conveniences
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [batch, seqlen, heads, headdim]")
+    B, N, Hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+        raise ValueError(f"shape mismatch q={tuple(q.shape)} k={tuple(k.shape)} v={tuple(v.shape)}")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+    return B, N, Hq, k.shape[2], d
+
+
+def forward(q, k, v, causal=False, window=0, scale=None, out=None, lse=None, stream=None):
+    """O, LSE = attention(q, k, v); bf16 or fp32 tensors in [B, N, H, d] layout."""
+    B, N, Hq, Hkv, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    if q.dtype == torch.bfloat16:
+        _check(fa_fwd(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, stream))
+    elif q.dtype == torch.float32:
+        _check(fa_fwd_fp32(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, stream))
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    return out, lse
+
+
+def workspace_for(B, Hq, Hkv, N, d, causal, window, device) -> torch.Tensor:
+    nbytes = fa_bwd_workspace_size(B, Hq, Hkv, N, d, causal, window)
+    if nbytes == 0:
+        raise FaError(FA_ERR_INVALID_ARG, fa_last_error())
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def backward(q, k, v, o, dO, lse, causal=False, window=0, scale=None, dq=None, dk=None,
+             dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of L = sum(O * dO) for bf16 tensors."""
+    B, N, Hq, Hkv, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = workspace_for(B, Hq, Hkv, N, d, causal, window, q.device)
+    _check(fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
+                  workspace, workspace.numel() * workspace.element_size(), stream))
+    return dq, dk, dv
+
+
+def dvec_from_workspace(workspace: torch.Tensor, B: int, Hq: int, N: int) -> torch.Tensor:
+    """View of D = rowsum(dO * O) ([B, Hq, N] float32) at the start of the workspace."""
+    return workspace[: B * Hq * N * 4].view(torch.float32).view(B, Hq, N)

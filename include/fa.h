@@ -1,0 +1,116 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact tiled scaled-dot-product attention on MI355X (gfx950).
+ *
+ * The operation (ainews.cool, "flash-attention transformer optimization", technical deep
+ * dive): O = Softmax(S) V with S = scale * Q K^T, computed without materialising the
+ * N x N matrix S in device memory.  The softmax runs block by block with a running row
+ * maximum and running normaliser (same page, same section, last paragraph; bmjup.com,
+ * "FlashAttention-2 ... 实战解析", section 2.2: numerator and denominator kept apart and
+ * combined only at the end).  The backward pass recomputes the probability matrix from
+ * Q, K and the stored per-row logsumexp instead of storing it (ainews.cool page, technical
+ * deep dive, item 2 "recomputation").
+ *
+ * Layout (bmjup.com page, section 4, usage example: (batch, seqlen, nheads, headdim)):
+ *   q, o, dO, dq : [B, N, Hq,  d]  contiguous, row-major ("BSHD")
+ *   k, v, dk, dv : [B, N, Hkv, d]  contiguous, row-major
+ *   lse          : [B, Hq, N]      float32, natural log: lse[i] = ln sum_j exp(s_ij)
+ * Query head hq reads KV head hq / (Hq / Hkv): consecutive groups of Hq/Hkv query heads
+ * share one KV head (MQA/GQA, hysenlabs.com "dao-ailab flash-attention", hardware-boundary
+ * section).
+ *
+ * Masks (bmjup.com page, sections 2.3 and 3.3):
+ *   causal != 0 : query row i attends keys j <= i
+ *   window  > 0 : query row i attends keys j >= i - window + 1 (a left bound; together
+ *                 with causal these are the `window` keys i-window+1 .. i)
+ *   window == 0 : no window
+ * A masked entry has probability zero: it never enters the normaliser.
+ *
+ * Conventions for every entry point:
+ *   - The caller owns every buffer (device memory, e.g. from hipMalloc or a framework
+ *     allocator).  The library never allocates, frees or synchronises.
+ *   - Calls enqueue work on `stream` (a hipStream_t; NULL = the null stream) and return.
+ *     Results are valid once the stream has reached that point.
+ *   - Arguments are validated before anything is launched.  On a non-FA_OK status
+ *     nothing was enqueued and fa_last_error() describes the problem.
+ *   - Stateless and re-entrant; the only state is the thread-local error message.
+ *   - Output buffers must not alias input buffers.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, Hq % Hkv != 0, window < 0,
+                             non-finite scale, size product overflowing 2^31 elements   */
+  FA_ERR_UNSUPPORTED = 2, /* head dim outside {64, 128, 256}                             */
+  FA_ERR_WORKSPACE = 3,   /* fa_bwd workspace missing or smaller than required           */
+  FA_ERR_HIP = 4          /* the HIP runtime reported an error at launch                  */
+} fa_status;
+
+/*
+ * Forward, bfloat16 in and out, float32 accumulation.
+ *   q [B,N,Hq,d], k/v [B,N,Hkv,d] : inputs, device pointers to bfloat16
+ *   o [B,N,Hq,d]                  : output, bfloat16 (rounded to nearest even once)
+ *   lse [B,Hq,N]                  : output, float32 natural-log logsumexp of each row of S
+ *   scale                         : any finite float (1/sqrt(d) for standard attention)
+ * d must be 64, 128 or 256.  A row that attends no key (impossible with causal or
+ * window >= 1 masks) gets o = 0 and lse = -inf.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                 void* stream);
+
+/*
+ * Forward, float32 in and out (same contract and layouts as fa_fwd, every tensor float32).
+ * Dot products, softmax and accumulation are all float32.
+ */
+fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
+                      int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                      float scale, void* stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs for these sizes.  Linear in N:
+ *   [0, a)      D = rowsum(dO * O), float32 [B, Hq, N]             (a = 256-byte aligned)
+ *   [a, a + b)  dQ accumulator, float32 [B, N, Hq, d]
+ * Returns 0 for arguments fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int window);
+
+/*
+ * Backward of L = sum(O * dO) for bfloat16 tensors (analytic gradient of fa_fwd).
+ *   q, k, v        : the forward inputs
+ *   o, lse         : the forward outputs (o bfloat16, lse float32) for the same q, k, v,
+ *                    masks and scale
+ *   dO [B,N,Hq,d]  : upstream gradient, bfloat16
+ *   dq [B,N,Hq,d], dk/dv [B,N,Hkv,d] : outputs, bfloat16; dk and dv of a KV head are
+ *                    summed over the query heads of its group
+ *   workspace      : device buffer of at least fa_bwd_workspace_size(...) bytes, 256-byte
+ *                    aligned; its contents on entry are ignored and on return hold D and
+ *                    the float32 dQ accumulator (layout above)
+ * The pass computes D = rowsum(dO * O), recomputes P = exp(S - lse) block by block, and
+ * accumulates dV = P^T dO, dK = scale * dS^T Q with dS = P * (dO V^T - D), dQ = scale * dS K.
+ * dQ is accumulated with float32 atomic adds, so its low bits may vary between runs; dK
+ * and dV are deterministic.
+ */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+                 int N, int d, int causal, int window, float scale, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* Message for the last non-FA_OK status returned on this thread ("" if none). */
+const char* fa_last_error(void);
+
+/* Library version string. */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

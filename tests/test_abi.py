@@ -1,0 +1,100 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared entry point,
+validates arguments before launching anything, and sizes its workspace linearly in N."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_fa2_amd import fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(fa.lib_path()),
+                                reason="libfa.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.lib_path())
+    declared = _declared_functions()
+    assert set(declared) == set(fa.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_string():
+    assert "gfx950" in fa.fa_version()
+
+
+BAD_FWD = [
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(N=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(window=-2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=1 << 12, N=1 << 12, Hq=1 << 4, Hkv=1 << 4, d=128), fa.FA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("bad,status", BAD_FWD)
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_fp32"])
+def test_forward_validation(entry, bad, status):
+    args = dict(B=1, Hq=2, Hkv=2, N=16, d=64, causal=0, window=0, scale=0.125)
+    args.update(bad)
+    fake = 256  # never dereferenced: validation fails before any launch
+    fn = getattr(fa, entry)
+    st = fn(fake, fake, fake, fake, fake, args["B"], args["Hq"], args["Hkv"], args["N"],
+            args["d"], args["causal"], args["window"], args["scale"], stream=0)
+    assert st == status
+    assert fa.fa_last_error().startswith(entry)
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd", "fa_fwd_fp32"])
+def test_forward_null_pointer(entry):
+    st = getattr(fa, entry)(None, 256, 256, 256, 256, 1, 1, 1, 8, 64, 0, 0, 0.1, stream=0)
+    assert st == fa.FA_ERR_INVALID_ARG
+    assert "null" in fa.fa_last_error()
+
+
+def test_backward_validation_and_workspace():
+    fake = 256
+    base = (1, 4, 2, 128, 128, 1, 0)
+    need = fa.fa_bwd_workspace_size(*base)
+    assert need > 0
+    # too small a workspace is rejected before launch
+    st = fa.fa_bwd(fake, fake, fake, fake, fake, fake, fake, fake, fake, 1, 4, 2, 128, 128, 1, 0,
+                   0.1, 4096, need - 1, stream=0)
+    assert st == fa.FA_ERR_WORKSPACE
+    st = fa.fa_bwd(fake, fake, fake, fake, fake, fake, fake, fake, fake, 1, 4, 2, 128, 128, 1, 0,
+                   0.1, None, need, stream=0)
+    assert st == fa.FA_ERR_WORKSPACE
+    # misaligned workspace
+    st = fa.fa_bwd(fake, fake, fake, fake, fake, fake, fake, fake, fake, 1, 4, 2, 128, 128, 1, 0,
+                   0.1, 4096 + 16, need, stream=0)
+    assert st == fa.FA_ERR_WORKSPACE
+    st = fa.fa_bwd(fake, fake, fake, fake, None, fake, fake, fake, fake, 1, 4, 2, 128, 128, 1, 0,
+                   0.1, 4096, need, stream=0)
+    assert st == fa.FA_ERR_INVALID_ARG
+    st = fa.fa_bwd(fake, fake, fake, fake, fake, fake, fake, fake, fake, 1, 4, 3, 128, 128, 1, 0,
+                   0.1, 4096, need, stream=0)
+    assert st == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_bwd_workspace_size(1, 4, 3, 128, 128, 1, 0) == 0
+
+
+def test_workspace_linear_in_n():
+    sizes = [fa.fa_bwd_workspace_size(2, 8, 2, n, 128, 1, 0) for n in (1024, 2048, 4096)]
+    # D (B*Hq*N*4, 256-aligned) + dQ accumulator (B*N*Hq*d*4)
+    for n, s in zip((1024, 2048, 4096), sizes):
+        assert s == ((2 * 8 * n * 4 + 255) // 256) * 256 + 2 * n * 8 * 128 * 4
+    assert sizes[2] - sizes[1] == 2 * (sizes[1] - sizes[0])
