@@ -1,0 +1,256 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the exact-attention hot path (forward + recompute backward).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one forward (fa_fwd) and one backward (fa_bwd) over one batch of the workload,
+with every input already resident in device memory.  The timed region is bracketed by
+torch.cuda.synchronize(); per-launch kernel durations come from HIP events recorded on the
+stream the kernels run on.  Prints ONE JSON line.
+
+FLOP convention (algorithmic, independent of how the kernels schedule the work):
+  forward  = 4 * B * Hq * pairs * d, pairs = N^2 (full), N^2 / 2 (causal),
+             W (W + 1) / 2 + (N - W) W (causal with a W-key window)
+  backward = 2.5 x forward (five products per attended pair: S, dP, dV, dK, dQ)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak (256 CU x 2.4 GHz x 4096)
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def attended_pairs(N: int, causal: bool, window: int) -> float:
+    """(query, key) pairs one head attends, with the metric's convention for causal."""
+    if not causal and window <= 0:
+        return float(N) * N
+    if causal and window <= 0:
+        return N * N / 2.0  # the metric's "halved for causal" convention
+    if causal:
+        W = min(window, N)
+        return W * (W + 1) / 2.0 + (N - W) * W
+    # left bound only: row i sees keys max(0, i - W + 1) .. N - 1
+    return float(sum(N - max(0, i - window + 1) for i in range(N)))
+
+
+def fwd_flops(w) -> float:
+    return 4.0 * w.B * w.Hq * attended_pairs(w.N, w.causal, w.window) * w.d
+
+
+def _src_sha(name: str) -> str:
+    p = os.path.join(ROOT, "exact_io_aware_fa2_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str, workload: str, source: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, or None when the
+    kernel source changed since the counters were taken."""
+    p = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        with open(p) as f:
+            rec = json.load(f).get(f"{kernel}@{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != _src_sha(source):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, do, max_workers: int = 16):
+    """Time the float64 oracle on a bounded sample of (batch, head) pairs of the same
+    inputs on the host cores; report algorithmic TFLOP/s with the same FLOP convention."""
+    import numpy as np
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
+    import oracle.attention as oa
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    workers = max(1, min(max_workers, cores))
+    per_head_f = fwd_flops(w) / (w.B * w.Hq)
+    bwd = do is not None
+    # about 10-30 s of work: ~3 heads per worker at the headline size, fewer if larger
+    est_head_s = per_head_f * (3.5 if bwd else 1.0) / 15e9
+    per_worker = max(1, min(4, int(12.0 / max(est_head_s, 1e-3))))
+    n_heads = min(w.B * w.Hq, workers * per_worker)
+    g = w.Hq // w.Hkv
+    pairs = [(i // w.Hq, i % w.Hq) for i in range(n_heads)]
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    tasks = []
+    for b, h in pairs:
+        qh, kh, vh = f64(q[b, :, h]), f64(k[b, :, h // g]), f64(v[b, :, h // g])
+        if bwd:
+            tasks.append((qh, kh, vh, f64(do[b, :, h]), w.causal, w.window, w.scale,
+                          oa.DEFAULT_ROW_CHUNK))
+        else:
+            tasks.append((qh, kh, vh, w.causal, w.window, w.scale, oa.DEFAULT_ROW_CHUNK))
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx,
+                             initializer=oa._limit_blas_threads) as ex:
+        # start every worker before the clock runs
+        list(ex.map(oa.default_workers, range(workers)))
+        t0 = time.perf_counter()
+        if bwd:
+            fwd_tasks = [t[:3] + t[4:] for t in tasks]
+            list(ex.map(oa._fwd_task, fwd_tasks))
+            list(ex.map(oa._bwd_task, tasks))
+        else:
+            list(ex.map(oa._fwd_task, tasks))
+        dt = time.perf_counter() - t0
+    flop = per_head_f * n_heads * (3.5 if bwd else 1.0)
+    return {
+        "value": flop / dt / 1e12,
+        "unit": "TFLOP/s (fwd+bwd, algorithmic)" if bwd else "TFLOP/s (fwd, algorithmic)",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"{n_heads} of {w.B * w.Hq} (batch, head) pairs of {w.name}, "
+                  f"{'forward + backward' if bwd else 'forward'}, float64 NumPy, "
+                  f"{workers} worker processes x 1 BLAS thread, {dt:.1f} s wall",
+        "seconds": dt,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None, help="workload name (default: headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                          "(the hot path shards over (batch, head) pairs, see DESIGN.md)"}))
+        return 2
+
+    import torch
+    from exact_io_aware_fa2_amd import fa
+    from exact_io_aware_fa2_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload or HEADLINE]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    q, k, v, do = make_inputs(w, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.N), device=dev, dtype=torch.float32)
+    bwd = do is not None and w.dtype == "bf16"
+    if bwd:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = fa.workspace_for(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, dev)
+        ws_bytes = ws.numel()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    fwd_fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_fp32
+
+    def run_fwd():
+        st = fwd_fn(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, w.scale, sh)
+        if st != fa.FA_OK:
+            raise RuntimeError(fa.fa_last_error())
+
+    def run_bwd():
+        st = fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal,
+                       w.window, w.scale, ws, ws_bytes, sh)
+        if st != fa.FA_OK:
+            raise RuntimeError(fa.fa_last_error())
+
+    for _ in range(args.warmup):
+        run_fwd()
+        if bwd:
+            run_bwd()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    for e in ev:  # torch creates the HIP event at its first record; the hook needs handles
+        e[4].record(stream)
+        e[5].record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        e = ev[s]
+        e[0].record(stream)
+        run_fwd()
+        e[1].record(stream)
+        if bwd:
+            fa.fa_bwd_time_main_kernel(e[4], e[5])
+            e[2].record(stream)
+            run_bwd()
+            e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    ms_step = wall * 1e3 / K
+    F = fwd_flops(w)
+    total_flop = F * (3.5 if bwd else 1.0)
+    out = {
+        "metric": "attention fwd & fwd+bwd TFLOPs/s (bf16, d=128, N=8K causal); % of MFMA peak",
+        "value": total_flop / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s (fwd+bwd)" if bwd else "TFLOP/s (fwd)",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0, sigma^2) draws, rounded to the compute dtype)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "window": w.window, "scale": w.scale},
+    }
+    avg = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    fwd_avg = avg(fwd_ms)
+    out["fwd_ms"] = fwd_avg
+    out["fwd_tflops"] = F / (fwd_avg * 1e-3) / 1e12
+    out["fwd_frac_of_peak"] = out["fwd_tflops"] / MFMA_BF16_PEAK_TFLOPS
+    kernels = {"fwd_bf16_kernel": (fwd_avg, F, "fa_fwd.hip")}
+    if bwd:
+        bwd_ms = [e[2].elapsed_time(e[3]) for e in ev]
+        main_ms = [e[4].elapsed_time(e[5]) for e in ev]
+        out["bwd_ms"] = avg(bwd_ms)
+        out["bwd_main_kernel_ms"] = avg(main_ms)
+        out["fwd_bwd_tflops_kernels"] = total_flop / ((fwd_avg + avg(bwd_ms)) * 1e-3) / 1e12
+        out["fwd_bwd_frac_of_peak"] = out["value"] / MFMA_BF16_PEAK_TFLOPS
+        kernels["bwd_bf16_kernel"] = (avg(main_ms), 2.5 * F, "fa_bwd.hip")
+    if w.dtype == "bf16":
+        name = max(kernels, key=lambda n: kernels[n][0])
+        ms, flop, src = kernels[name]
+        achieved = flop / (ms * 1e-3) / 1e12
+        out["roofline"] = {
+            "kernel": name,
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": _traffic(name, w.name, src),
+            "avg_launch_ms": ms,
+        }
+    out["context"] = ("pages' A100 figures at 16K tokens (other hardware, not a target): "
+                      "~50 TFLOP/s standard PyTorch attention vs >180 TFLOP/s FlashAttention-2")
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do if bwd else None)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

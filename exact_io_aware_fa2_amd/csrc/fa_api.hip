@@ -17,6 +17,8 @@
 namespace {
 
 thread_local char g_err[512] = "";
+thread_local hipEvent_t g_time_start = nullptr;  // pending fa_bwd_time_main_kernel request
+thread_local hipEvent_t g_time_stop = nullptr;
 
 fa_status fail(fa_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 fa_status fail(fa_status st, const char* fmt, ...) {
@@ -114,8 +116,18 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   float* dvec = reinterpret_cast<float*>(ws);
   float* dq_acc = reinterpret_cast<float*>(ws + align256((size_t)B * Hq * N * sizeof(float)));
   fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dvec, dq_acc, B, Hq, Hkv, N, d,
-                causal ? 1 : 0, window, scale, scale * fa::kHostLog2e};
+                causal ? 1 : 0, window, scale, scale * fa::kHostLog2e, g_time_start,
+                g_time_stop};
+  g_time_start = g_time_stop = nullptr;
   return launched("fa_bwd", fa::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+fa_status fa_bwd_time_main_kernel(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd_time_main_kernel: give both events or neither");
+  g_time_start = static_cast<hipEvent_t>(start_event);
+  g_time_stop = static_cast<hipEvent_t>(stop_event);
+  return ok();
 }
 
 const char* fa_last_error(void) { return g_err; }

@@ -369,6 +369,10 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int num_kb = (a.N + Cfg::BKN - 1) / Cfg::BKN;
   const int grid = a.B * a.Hkv * num_kb * Cfg::NSPLIT;
+  if (a.ev_start) {
+    e = hipEventRecord(a.ev_start, st);
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(bwd_bf16_kernel<D>, dim3(grid), dim3(256), Cfg::LDS_BYTES, st,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
                      (const bf16_t*)a.dO, a.lse, a.dvec, a.dq_acc, (bf16_t*)a.dk,
@@ -376,6 +380,10 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
                      a.c_log2_signed, a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.ev_stop) {
+    e = hipEventRecord(a.ev_stop, st);
+    if (e != hipSuccess) return e;
+  }
   const long n8 = rows * D / 8;
   hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
                      a.dq_acc, (bf16_t*)a.dq, n8, a.scale);

@@ -36,6 +36,8 @@ struct BwdArgs {
   int B, Hq, Hkv, N, d, causal, window;
   float scale;
   float c_log2_signed;  // scale * log2(e)
+  hipEvent_t ev_start;  // optional events recorded around the main kernel (may be null)
+  hipEvent_t ev_stop;
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);

@@ -21,8 +21,8 @@ _lib = None
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_bwd_workspace_size", "fa_last_error",
-            "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_bwd_workspace_size",
+            "fa_bwd_time_main_kernel", "fa_last_error", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -53,6 +53,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_bwd_time_main_kernel.argtypes = [vp, vp]
+    lib.fa_bwd_time_main_kernel.restype = i
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -102,6 +104,16 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, sc
     return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq),
                          _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal), int(window),
                          float(scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_bwd_time_main_kernel(start_event, stop_event) -> int:
+    """Ask the next fa_bwd on this thread to record the two torch.cuda.Event objects (or
+    raw hipEvent_t handles) around its main kernel."""
+    def handle(e):
+        if e is None or isinstance(e, int):
+            return e
+        return e.cuda_event
+    return load().fa_bwd_time_main_kernel(handle(start_event), handle(stop_event))
 
 
 def fa_last_error() -> str:

@@ -103,6 +103,15 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int N, int d, int causal, int window, float scale, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/*
+ * Benchmark hook (no counterpart on the pages): the next fa_bwd call made on this thread
+ * records `start_event` on its stream right before its main recompute kernel and
+ * `stop_event` right after it, so a caller can time that kernel alone with
+ * hipEventElapsedTime.  Arguments are hipEvent_t handles owned by the caller; passing NULL
+ * for both clears a pending request.  Returns FA_ERR_INVALID_ARG if exactly one is NULL.
+ */
+fa_status fa_bwd_time_main_kernel(void* start_event, void* stop_event);
+
 /* Message for the last non-FA_OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);
 

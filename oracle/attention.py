@@ -281,7 +281,7 @@ def _run(tasks, fn, workers):
         return list(ex.map(fn, tasks))
 
 
-def default_workers() -> int:
+def default_workers(_=None) -> int:
     try:
         return len(os.sched_getaffinity(0))
     except AttributeError:
