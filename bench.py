@@ -224,12 +224,19 @@ def main() -> int:
     kernels = {"fwd_bf16_kernel": (fwd_avg, F, "fa_fwd.hip")}
     if bwd:
         bwd_ms = [e[2].elapsed_time(e[3]) for e in ev]
-        main_ms = [e[4].elapsed_time(e[5]) for e in ev]
+        pre_ms = [e[2].elapsed_time(e[4]) for e in ev]   # D = rowsum(dO * O)
+        kv_ms = [e[4].elapsed_time(e[5]) for e in ev]    # key-block kernel: dK, dV
+        q_ms = [e[5].elapsed_time(e[3]) for e in ev]     # query-block kernel: dQ
         out["bwd_ms"] = avg(bwd_ms)
-        out["bwd_main_kernel_ms"] = avg(main_ms)
+        out["bwd_pre_ms"] = avg(pre_ms)
+        out["bwd_dkdv_kernel_ms"] = avg(kv_ms)
+        out["bwd_dq_kernel_ms"] = avg(q_ms)
         out["fwd_bwd_tflops_kernels"] = total_flop / ((fwd_avg + avg(bwd_ms)) * 1e-3) / 1e12
         out["fwd_bwd_frac_of_peak"] = out["value"] / MFMA_BF16_PEAK_TFLOPS
-        kernels["bwd_bf16_kernel"] = (avg(main_ms), 2.5 * F, "fa_bwd.hip")
+        # algorithmic products executed by each kernel: dK/dV kernel S, dP, dV, dK (4 per
+        # pair, 2x the forward); dQ kernel S, dP, dQ (3 per pair, 1.5x the forward)
+        kernels["bwd_dkdv_kernel"] = (avg(kv_ms), 2.0 * F, "fa_bwd.hip")
+        kernels["bwd_dq_kernel"] = (avg(q_ms), 1.5 * F, "fa_bwd.hip")
     if w.dtype == "bf16":
         name = max(kernels, key=lambda n: kernels[n][0])
         ms, flop, src = kernels[name]

@@ -73,8 +73,13 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "fa_fwd: null pointer");
   fa_status st = check_common("fa_fwd", B, Hq, Hkv, N, d, causal, window, scale);
   if (st != FA_OK) return st;
-  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal ? 1 : 0, window,
-                fabsf(scale) * fa::kHostLog2e, scale * fa::kHostLog2e, scale < 0.f ? 1 : 0};
+  // The bf16 kernel works with the non-negative log2 scale |scale| log2(e) (a negative scale
+  // negates Q exactly) and marks masked scores with -inf; for scale == 0 it gets a tiny
+  // positive value instead of 0 so that -inf * scale stays -inf (every unmasked weight still
+  // rounds to exactly 1).
+  const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal ? 1 : 0, window, c2,
+                scale * fa::kHostLog2e, scale < 0.f ? 1 : 0};
   return launched("fa_fwd", fa::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
@@ -93,9 +98,7 @@ fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, 
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int window) {
   if (check_common("fa_bwd_workspace_size", B, Hq, Hkv, N, d, causal, window, 1.f) != FA_OK)
     return 0;
-  const size_t dvec = align256((size_t)B * Hq * N * sizeof(float));
-  const size_t dqacc = (size_t)B * N * Hq * d * sizeof(float);
-  return dvec + dqacc;
+  return align256((size_t)B * Hq * N * sizeof(float));
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -112,10 +115,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                 workspace ? workspace_bytes : (size_t)0);
   if (((uintptr_t)workspace & 255) != 0)
     return fail(FA_ERR_WORKSPACE, "fa_bwd: workspace must be 256-byte aligned");
-  char* ws = static_cast<char*>(workspace);
-  float* dvec = reinterpret_cast<float*>(ws);
-  float* dq_acc = reinterpret_cast<float*>(ws + align256((size_t)B * Hq * N * sizeof(float)));
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dvec, dq_acc, B, Hq, Hkv, N, d,
+  float* dvec = static_cast<float*>(workspace);
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dvec, B, Hq, Hkv, N, d,
                 causal ? 1 : 0, window, scale, scale * fa::kHostLog2e, g_time_start,
                 g_time_stop};
   g_time_start = g_time_stop = nullptr;

@@ -3,60 +3,47 @@
 // The backward recomputes the probability matrix block by block from Q, K and the
 // stored logsumexp instead of reading a stored N x N matrix (ainews.cool, "flash-attention
 // transformer optimization", technical deep dive, item 2).  With L = sum(O * dO):
-//   D_i   = sum_c dO_ic O_ic                       (preprocess kernel)
+//   D_i   = sum_c dO_ic O_ic                                   (preprocess kernel)
 //   P_ij  = exp(s_ij - LSE_i),  dP_ij = dO_i . v_j,  dS_ij = P_ij (dP_ij - D_i)
-//   dV_j  = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i = scale sum_j dS_ij k_j
+//   dV_j  = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i      (key-block kernel)
+//   dQ_i  = scale sum_j dS_ij k_j                               (query-block kernel)
 //
-// Main kernel: one workgroup = 4 waves = 128 keys of one (batch, KV head) (32 keys per
-// wave), optionally one half of the head dim for the accumulated outputs when d = 256.
-//   * the wave's K and V rows sit in VGPRs as the B operands of S = Q K^T and dP = dO V^T;
-//     every lane holds one key and 16 rows per 32 x 32 tile;
-//   * Q, dO (64 rows), their LSE and D go through LDS; the next block's rows are loaded
-//     into registers while the current block computes;
-//   * P and dS (accumulator layout) feed dV^T += dO^T P and dK^T += Q^T dS directly as B
-//     operands; dO^T and Q^T come from LDS with the transposing ds_read_b64_tr_b16;
-//   * dK/dV accumulate in registers across every query head of the GQA group and every
-//     query block, then are written once (no atomics on dK/dV);
-//   * dS^T is shared through LDS and each wave forms a slice of dQ = dS K over all 128
-//     keys, added into a float32 accumulator with hardware float atomics (lanes run along
-//     the head dim, so each atomic instruction touches two 128-byte lines); a last kernel
-//     scales and rounds the accumulator to bf16.
+// Two main kernels instead of one with atomics.  On this chip a CU's LDS serves about one
+// 16-byte operand read per 32x32x16 MFMA, so every product reads its LDS operand with one
+// ds_read_b128: operands that must be contiguous along the reduced index (Q^T and dO^T for
+// dK/dV, K^T for dQ) are transposed once while being staged (register packing, see
+// store_4x8_transposed), never with per-use transposing reads.  Recomputing S and dP in the
+// query-block kernel costs two extra products per tile pair but removes the float32 dQ
+// accumulator, its atomics and its conversion pass, and keeps dQ deterministic.
+//
+// Key-block kernel: a workgroup = 4 waves = 128 keys of one (batch, KV head) (32 keys per
+// wave; for d = 256 one half of the head dim of dK/dV).  The wave's K and V rows are MFMA B
+// operands in VGPRs; dK^T and dV^T accumulate in registers across every query head of the
+// GQA group and every query block, and are written once.
+//
+// Query-block kernel: a workgroup = 8 waves (d <= 128) or 4 waves = 32 query rows per wave,
+// the same shape as the forward: Q and dO rows are B operands in VGPRs, K, V and K^T tiles
+// stream through double-buffered LDS, and S^T / dP^T put one query row in each lane so LSE
+// and D are per-lane scalars and dS^T feeds dQ^T += K^T dS^T straight from the accumulator.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
 
-template <int D>
-struct BwdCfg {
-  static constexpr int BKN = 128;                // keys per workgroup
-  static constexpr int BQ = 64;                  // query rows per inner step
-  static constexpr int DH = D <= 128 ? D : 128;  // head-dim slice of dK/dV/dQ per workgroup
-  static constexpr int NSPLIT = D / DH;
-  static constexpr int STR = D + 8;              // sQ / sdO row stride (elements)
-  static constexpr int KSTR = DH + 8;            // sK row stride
-  static constexpr int SSTR = BQ + 8;            // sdS row stride, [key][row] layout
-  static constexpr bool PREFETCH = D <= 128;     // register budget allows prefetching
-  static constexpr int SK_BYTES = BKN * KSTR * 2;
-  static constexpr int SQ_BYTES = BQ * STR * 2;
-  static constexpr int SS_BYTES = BKN * SSTR * 2;
-  static constexpr int LDS_BYTES = SK_BYTES + 2 * SQ_BYTES + SS_BYTES + 2 * BQ * 4;
-};
-
-__device__ __forceinline__ bool allowed(int row, int key, int N, int causal, int window) {
-  return key < N && (!causal || key <= row) && (window <= 0 || key >= row - window + 1);
-}
-
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// D = rowsum(dO * O) in float32 from the stored bf16 O, and clears the dQ accumulator.
-// D/8 threads per (batch, row, head) row, 16 bytes each.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, to_bf16x2(a, b));
+}
+
+// D = rowsum(dO * O) in float32 from the stored bf16 O.  D/8 threads per (batch, row, head)
+// row, 16 bytes each.
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ O,
                                                       const bf16_t* __restrict__ dO,
-                                                      float* __restrict__ Dv,
-                                                      float* __restrict__ dq_acc, int B,
-                                                      int Hq, int N) {
+                                                      float* __restrict__ Dv, int B, int Hq,
+                                                      int N) {
   constexpr int T = D / 8, RPB = 256 / T;
   const long total = (long)B * N * Hq;
   const long r = (long)blockIdx.x * RPB + threadIdx.x / T;
@@ -69,9 +56,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__
     sum += bf_lo(o.y) * bf_lo(g.y) + bf_hi(o.y) * bf_hi(g.y);
     sum += bf_lo(o.z) * bf_lo(g.z) + bf_hi(o.z) * bf_hi(g.z);
     sum += bf_lo(o.w) * bf_lo(g.w) + bf_hi(o.w) * bf_hi(g.w);
-    float4* z = reinterpret_cast<float4*>(dq_acc + r * D + t * 8);
-    z[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-    z[1] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int off = T / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
@@ -83,28 +67,37 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__
   }
 }
 
+// =====================================================================================
+// dK / dV
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
+struct KVCfg {
+  static constexpr int NT = 256;                 // 4 waves x 32 keys
+  static constexpr int BKN = 128;                // keys per workgroup
+  static constexpr int DH = D <= 128 ? D : 128;  // head-dim slice of dK/dV per workgroup
+  static constexpr int NSPLIT = D / DH;
+  static constexpr int BQ = D <= 128 ? 64 : 32;  // query rows per step
+  static constexpr int MT = BQ / 32;             // 32-row MFMA tiles per step
+  static constexpr int STR = D + 8;              // row-major Q / dO row stride (elements)
+  static constexpr int TSTR = BQ + 8;            // transposed Q^T / dO^T row stride
+  static constexpr int SQ = BQ * STR;
+  static constexpr int SQT = DH * TSTR;
+  static constexpr int BUF = 2 * SQ + 2 * SQT;   // Q, dO, Q^T, dO^T (elements)
+  static constexpr int LDS_BYTES = 2 * (BUF * 2 + 2 * BQ * 4);  // + LSE, D; double buffered
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    float* __restrict__ dq_acc, bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int B,
-    int Hq, int Hkv, int N, int causal, int window, float c, float scale) {
-  using Cfg = BwdCfg<D>;
-  constexpr int BKN = Cfg::BKN, BQ = Cfg::BQ, DH = Cfg::DH, NSPLIT = Cfg::NSPLIT;
-  constexpr int STR = Cfg::STR, KSTR = Cfg::KSTR, SSTR = Cfg::SSTR;
-  constexpr bool PREFETCH = Cfg::PREFETCH;
-  constexpr int NC = D / 16;     // k-steps of S and dP over the head dim
-  constexpr int NDH = DH / 32;   // owned 32-wide head-dim tiles of dK^T / dV^T / dQ
-  constexpr int TPW = DH / 64;   // dQ tiles per wave (NDH d-tiles x 2 row tiles / 4 waves)
-  static_assert(TPW >= 1, "head dim slice too small");
-
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
+    int causal, int window, float c, float scale) {
+  using Cfg = KVCfg<D>;
+  constexpr int BKN = Cfg::BKN, BQ = Cfg::BQ, MT = Cfg::MT, DH = Cfg::DH;
+  constexpr int NSPLIT = Cfg::NSPLIT, STR = Cfg::STR, TSTR = Cfg::TSTR;
+  constexpr int NC = D / 16;    // k-steps of S and dP over the head dim
+  constexpr int NDH = DH / 32;  // owned 32-wide head-dim tiles of dK^T / dV^T
+  constexpr int BUFB = Cfg::BUF * 2 + 2 * BQ * 4;  // bytes per buffer
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16_t* sK = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + Cfg::SK_BYTES);
-  bf16_t* sdO = reinterpret_cast<bf16_t*>(smem + Cfg::SK_BYTES + Cfg::SQ_BYTES);
-  bf16_t* sdS = reinterpret_cast<bf16_t*>(smem + Cfg::SK_BYTES + 2 * Cfg::SQ_BYTES);
-  float* sL = reinterpret_cast<float*>(smem + Cfg::SK_BYTES + 2 * Cfg::SQ_BYTES + Cfg::SS_BYTES);
-  float* sD = sL + BQ;
 
   const int num_kb = (N + BKN - 1) / BKN;
   const int total = B * Hkv * num_kb * NSPLIT;
@@ -119,9 +112,8 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
   const int G = Hq / Hkv;
   const int dh0 = split * DH;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int hh = lane >> 5, l32 = lane & 31;
-  const int grp = lane >> 4, j16 = lane & 15;
   const int n0 = kb * BKN, kw0 = n0 + 32 * w, key = kw0 + l32;
 
   const size_t qs = (size_t)Hq * D, ks = (size_t)Hkv * D;
@@ -130,27 +122,14 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
 
   // B operands K^T and V^T of this lane's key.
   bf16x8 kop[NC], vop[NC];
-  if (key < N) {
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      kop[cc] = __builtin_bit_cast(bf16x8, gload16(Kb + (size_t)key * ks + 16 * cc + 8 * hh));
-      vop[cc] = __builtin_bit_cast(bf16x8, gload16(Vb + (size_t)key * ks + 16 * cc + 8 * hh));
-    }
-  } else {
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      kop[cc] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-      vop[cc] = kop[cc];
-    }
-  }
-  // K slice [n0, n0 + 128) x [dh0, dh0 + DH) in LDS for the dQ product.
-  for (int ch = tid; ch < BKN * DH / 8; ch += 256) {
-    const int kl = ch / (DH / 8), dc = ch - kl * (DH / 8);
-    const int n = n0 + kl;
-    const uint4 val = n < N ? gload16(Kb + (size_t)n * ks + dh0 + dc * 8) : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(sK + kl * KSTR + dc * 8) = val;
+  for (int cc = 0; cc < NC; ++cc) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    kop[cc] = __builtin_bit_cast(bf16x8, key < N ? gload16(Kb + (size_t)key * ks + 16 * cc + 8 * hh) : z);
+    vop[cc] = __builtin_bit_cast(bf16x8, key < N ? gload16(Vb + (size_t)key * ks + 16 * cc + 8 * hh) : z);
   }
 
+  // query rows any key of this block can be attended by
   const int qb_lo = causal ? n0 / BQ : 0;
   const int row_end = window > 0 ? min(N, n0 + BKN + window - 1) : N;
   const int qb_hi = (row_end + BQ - 1) / BQ;
@@ -164,25 +143,25 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
     dv[i] = zero16();
   }
 
-  constexpr int QCPR = D / 8;           // 16-byte chunks per Q row
-  constexpr int QPT = BQ * QCPR / 256;  // chunks per thread
-  uint4 qreg[QPT], oreg[QPT];
+  // Staging: a task = 4 rows x 8 dims of Q and of dO, stored row-major and (for the owned
+  // head-dim slice) transposed.
+  constexpr int CPR = D / 8;
+  constexpr int TASKS = (BQ / 4) * CPR;
+  constexpr int PT = (TASKS + 255) / 256;
+  uint4 qr[PT][4], orr[PT][4];
   float lreg = 0.f, dreg = 0.f;
-  auto load_regs = [&](int it) {
+  auto gload = [&](int it) {
     const int g = it / nq, qb = qb_lo + (it - g * nq);
     const int hq = hkv * G + g, r0 = qb * BQ;
     const bf16_t* Qb = Q + ((size_t)b * N * Hq + hq) * D;
     const bf16_t* Ob = dO + ((size_t)b * N * Hq + hq) * D;
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int ch = tid + 256 * i, rr = ch / QCPR, dc = ch - rr * QCPR;
-      const int n = r0 + rr;
-      if (n < N) {
-        qreg[i] = gload16(Qb + (size_t)n * qs + dc * 8);
-        oreg[i] = gload16(Ob + (size_t)n * qs + dc * 8);
-      } else {
-        qreg[i] = make_uint4(0, 0, 0, 0);
-        oreg[i] = make_uint4(0, 0, 0, 0);
+    for (int p = 0; p < PT; ++p) {
+      const int task = tid + 256 * p;
+      if (TASKS % 256 == 0 || task < TASKS) {
+        const int rg = task / CPR, dc = task - rg * CPR;
+        load_4x8(qr[p], Qb, qs, r0 + 4 * rg, N, 8 * dc);
+        load_4x8(orr[p], Ob, qs, r0 + 4 * rg, N, 8 * dc);
       }
     }
     if (tid < BQ) {
@@ -192,68 +171,111 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
       dreg = n < N ? Dv[li] : 0.f;
     }
   };
-  auto store_regs = [&]() {
+  auto swrite = [&](int buf) {
+    bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + buf * BUFB);
+    bf16_t* sO = sQ + Cfg::SQ;
+    bf16_t* sQT = sO + Cfg::SQ;
+    bf16_t* sOT = sQT + Cfg::SQT;
+    float* sL = reinterpret_cast<float*>(sOT + Cfg::SQT);
 #pragma unroll
-    for (int i = 0; i < QPT; ++i) {
-      const int ch = tid + 256 * i, rr = ch / QCPR, dc = ch - rr * QCPR;
-      *reinterpret_cast<uint4*>(sQ + rr * STR + dc * 8) = qreg[i];
-      *reinterpret_cast<uint4*>(sdO + rr * STR + dc * 8) = oreg[i];
+    for (int p = 0; p < PT; ++p) {
+      const int task = tid + 256 * p;
+      if (TASKS % 256 == 0 || task < TASKS) {
+        const int rg = task / CPR, dc = task - rg * CPR;
+        store_4x8_rows(sQ, STR, 4 * rg, 8 * dc, qr[p]);
+        store_4x8_rows(sO, STR, 4 * rg, 8 * dc, orr[p]);
+        const int dl = 8 * dc - dh0;
+        if (NSPLIT == 1 || (dl >= 0 && dl < DH)) {
+          store_4x8_transposed(sQT, TSTR, 4 * rg, dl, qr[p]);
+          store_4x8_transposed(sOT, TSTR, 4 * rg, dl, orr[p]);
+        }
+      }
     }
     if (tid < BQ) {
       sL[tid] = lreg;
-      sD[tid] = dreg;
+      sL[BQ + tid] = dreg;
     }
   };
 
-  if (PREFETCH && total_it > 0) load_regs(0);
+  if (total_it > 0) {
+    gload(0);
+    swrite(0);
+    if (total_it > 1) gload(1);
+  }
+  __syncthreads();
   for (int it = 0; it < total_it; ++it) {
+    const int buf = it & 1;
+    const bf16_t* sQ = reinterpret_cast<const bf16_t*>(smem + buf * BUFB);
+    const bf16_t* sO = sQ + Cfg::SQ;
+    const bf16_t* sQT = sO + Cfg::SQ;
+    const bf16_t* sOT = sQT + Cfg::SQT;
+    const float* sL = reinterpret_cast<const float*>(sOT + Cfg::SQT);
+    const float* sD = sL + BQ;
     const int g = it / nq, qb = qb_lo + (it - g * nq);
-    const int hq = hkv * G + g, r0 = qb * BQ;
-    __syncthreads();
-    if (!PREFETCH) load_regs(it);
-    store_regs();
-    __syncthreads();
-    if (PREFETCH && it + 1 < total_it) load_regs(it + 1);
-
+    const int r0 = qb * BQ;
+    (void)g;
     const bool active = kw0 < N && (!causal || r0 + BQ - 1 >= kw0) &&
                         (window <= 0 || r0 <= kw0 + 31 + window - 1);
-    bf16_t* sdS_lane = sdS + (32 * w + l32) * SSTR + 4 * hh;
     if (active) {
-      const bool need_mask = (kw0 + 32 > N) || (causal && kw0 + 31 > r0) ||
-                             (window > 0 && kw0 < r0 + BQ - window);
-      f32x16 s[2], dp[2];
+      // S = Q K^T and dP = dO V^T for this wave's 32 keys (lane = key, rows in registers).
+      f32x16 s[MT], dp[MT];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        s[mt] = zero16();
-        dp[mt] = zero16();
+      for (int mt = 0; mt < MT; ++mt) {
         const bf16_t* qa = sQ + (32 * mt + l32) * STR + 8 * hh;
-        const bf16_t* oa = sdO + (32 * mt + l32) * STR + 8 * hh;
+        const bf16_t* oa = sO + (32 * mt + l32) * STR + 8 * hh;
+        bf16x8 qa_op[NC], oa_op[NC];
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-          s[mt] = mfma32(lds_read_b128(qa + 16 * cc), kop[cc], s[mt]);
-          dp[mt] = mfma32(lds_read_b128(oa + 16 * cc), vop[cc], dp[mt]);
+          qa_op[cc] = lds_read_b128(qa + 16 * cc);
+          oa_op[cc] = lds_read_b128(oa + 16 * cc);
+        }
+        s[mt] = zero16();
+        dp[mt] = zero16();
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          s[mt] = mfma32(qa_op[cc], kop[cc], s[mt]);
+          dp[mt] = mfma32(oa_op[cc], vop[cc], dp[mt]);
         }
       }
-      bf16x8 pP[2][2], pS[2][2];
+      // P = exp2(S c - LSE log2 e), masked entries 0 (selects under a wave-uniform branch).
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int rl0 = 32 * mt + 8 * g4 + 4 * hh;
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + rl0);
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(sD + rl0);
-          float pv[4], dsv[4];
+          const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + 32 * mt + 8 * g4 + 4 * hh);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g4 + e;
-            float pe = fast_exp2(fmaf(s[mt][r], c, -L4[e]));
-            if (need_mask && !allowed(r0 + rl0 + e, key, N, causal, window)) pe = 0.f;
-            pv[e] = pe;
-            dsv[e] = pe * (dp[mt][r] - D4[e]);
+          for (int e = 0; e < 4; ++e)
+            s[mt][4 * g4 + e] = fast_exp2(fmaf(s[mt][4 * g4 + e], c, -L4[e]));
+        }
+      }
+      const bool need_mask = (kw0 + 32 > N) || (causal && kw0 + 31 > r0) ||
+                             (window > 0 && kw0 < r0 + BQ - window);
+      if (need_mask) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = r0 + 32 * mt + (r >> 2) * 8 + hh * 4 + (r & 3);
+            const bool ok = (key < N) & (!causal | (key <= row)) &
+                            ((window <= 0) | (key >= row - window + 1));
+            s[mt][r] = ok ? s[mt][r] : 0.f;
           }
-          const bf16x2 p01 = to_bf16x2(pv[0], pv[1]), p23 = to_bf16x2(pv[2], pv[3]);
-          const bf16x2 d01 = to_bf16x2(dsv[0], dsv[1]), d23 = to_bf16x2(dsv[2], dsv[3]);
+        }
+      }
+      // dS = P (dP - D); pack P and dS as bf16 B operands (k = query row).
+      bf16x8 pP[MT][2], pS[MT][2];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 D4 = *reinterpret_cast<const f32x4*>(sD + 32 * mt + 8 * g4 + 4 * hh);
+          float dsv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dsv[e] = s[mt][4 * g4 + e] * (dp[mt][4 * g4 + e] - D4[e]);
           const int c2 = g4 >> 1, i0 = 4 * (g4 & 1);
+          const bf16x2 p01 = to_bf16x2(s[mt][4 * g4], s[mt][4 * g4 + 1]);
+          const bf16x2 p23 = to_bf16x2(s[mt][4 * g4 + 2], s[mt][4 * g4 + 3]);
+          const bf16x2 d01 = to_bf16x2(dsv[0], dsv[1]), d23 = to_bf16x2(dsv[2], dsv[3]);
           pP[mt][c2][i0] = p01[0];
           pP[mt][c2][i0 + 1] = p01[1];
           pP[mt][c2][i0 + 2] = p23[0];
@@ -262,55 +284,32 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
           pS[mt][c2][i0 + 1] = d01[1];
           pS[mt][c2][i0 + 2] = d23[0];
           pS[mt][c2][i0 + 3] = d23[1];
-          uint2 u;
-          u.x = __builtin_bit_cast(uint32_t, d01);
-          u.y = __builtin_bit_cast(uint32_t, d23);
-          *reinterpret_cast<uint2*>(sdS_lane + 32 * mt + 8 * g4) = u;
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the owned head-dim slice.
-      const int tr_off = (hh * 4 + (j16 >> 2)) * STR + dh0 + 16 * (grp & 1) + 4 * (j16 & 3);
+      // dV^T += dO^T P and dK^T += Q^T dS over the owned head-dim slice (A operands from
+      // the transposed tiles: the 8 rows of a k-step are contiguous).
 #pragma unroll
       for (int dt = 0; dt < NDH; ++dt) {
+        const bf16_t* oa = sOT + (32 * dt + l32) * TSTR + 8 * hh;
+        const bf16_t* qa = sQT + (32 * dt + l32) * TSTR + 8 * hh;
+        bf16x8 ao[2 * MT], aq[2 * MT];
 #pragma unroll
-        for (int kstep = 0; kstep < BQ / 16; ++kstep) {
-          const int off = tr_off + 16 * kstep * STR + 32 * dt;
-          const bf16x8 ao = lds_read_tr_x2(sdO + off, sdO + off + 8 * STR);
-          dv[dt] = mfma32(ao, pP[kstep >> 1][kstep & 1], dv[dt]);
-          const bf16x8 aq = lds_read_tr_x2(sQ + off, sQ + off + 8 * STR);
-          dk[dt] = mfma32(aq, pS[kstep >> 1][kstep & 1], dk[dt]);
+        for (int kstep = 0; kstep < 2 * MT; ++kstep) {
+          ao[kstep] = lds_read_b128(oa + 16 * kstep);
+          aq[kstep] = lds_read_b128(qa + 16 * kstep);
+        }
+#pragma unroll
+        for (int kstep = 0; kstep < 2 * MT; ++kstep) {
+          dv[dt] = mfma32(ao[kstep], pP[kstep >> 1][kstep & 1], dv[dt]);
+          dk[dt] = mfma32(aq[kstep], pS[kstep >> 1][kstep & 1], dk[dt]);
         }
       }
-    } else {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          *reinterpret_cast<uint2*>(sdS_lane + 32 * mt + 8 * g4) = make_uint2(0, 0);
+    }
+    if (it + 1 < total_it) {
+      swrite(buf ^ 1);
+      if (it + 2 < total_it) gload(it + 2);
     }
     __syncthreads();
-
-    // dQ[rows][d] (slice) = dS[rows][128 keys] K[128 keys][d]; lanes run along d.
-#pragma unroll
-    for (int u = 0; u < TPW; ++u) {
-      const int tile = w * TPW + u, dt = tile % NDH, rt = tile / NDH;
-      f32x16 a = zero16();
-#pragma unroll
-      for (int kstep = 0; kstep < BKN / 16; ++kstep) {
-        const int key0 = 16 * kstep + 8 * hh + (j16 >> 2);
-        const bf16_t* sp = sdS + key0 * SSTR + 32 * rt + 16 * (grp & 1) + 4 * (j16 & 3);
-        const bf16_t* kp = sK + key0 * KSTR + 32 * dt + 16 * (grp & 1) + 4 * (j16 & 3);
-        const bf16x8 as = lds_read_tr_x2(sp, sp + 4 * SSTR);
-        const bf16x8 bk = lds_read_tr_x2(kp, kp + 4 * KSTR);
-        a = mfma32(as, bk, a);
-      }
-      float* dqb = dq_acc + ((size_t)b * N * Hq + hq) * D + dh0 + 32 * dt + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = r0 + 32 * rt + (r >> 2) * 8 + hh * 4 + (r & 3);
-        if (n < N) unsafeAtomicAdd(dqb + (size_t)n * qs, a[r]);
-      }
-    }
   }
 
   if (key < N) {
@@ -322,71 +321,282 @@ __global__ __launch_bounds__(256, 1) void bwd_bf16_kernel(
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d = 32 * dt + 8 * g4 + 4 * hh;
         uint2 u;
-        u.x = __builtin_bit_cast(uint32_t, to_bf16x2(dk[dt][4 * g4] * scale, dk[dt][4 * g4 + 1] * scale));
-        u.y = __builtin_bit_cast(uint32_t, to_bf16x2(dk[dt][4 * g4 + 2] * scale, dk[dt][4 * g4 + 3] * scale));
+        u.x = pack_bf16(dk[dt][4 * g4] * scale, dk[dt][4 * g4 + 1] * scale);
+        u.y = pack_bf16(dk[dt][4 * g4 + 2] * scale, dk[dt][4 * g4 + 3] * scale);
         *reinterpret_cast<uint2*>(dkr + d) = u;
-        u.x = __builtin_bit_cast(uint32_t, to_bf16x2(dv[dt][4 * g4], dv[dt][4 * g4 + 1]));
-        u.y = __builtin_bit_cast(uint32_t, to_bf16x2(dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3]));
+        u.x = pack_bf16(dv[dt][4 * g4], dv[dt][4 * g4 + 1]);
+        u.y = pack_bf16(dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3]);
         *reinterpret_cast<uint2*>(dvr + d) = u;
       }
     }
   }
 }
 
-// dQ = scale * accumulator, rounded once to bf16.  8 elements per thread.
-__global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc,
-                                                         bf16_t* __restrict__ dq, long n8,
-                                                         float scale) {
-  const long i = (long)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const float4 a = reinterpret_cast<const float4*>(acc)[2 * i];
-  const float4 bq = reinterpret_cast<const float4*>(acc)[2 * i + 1];
-  uint4 u;
-  u.x = __builtin_bit_cast(uint32_t, to_bf16x2(a.x * scale, a.y * scale));
-  u.y = __builtin_bit_cast(uint32_t, to_bf16x2(a.z * scale, a.w * scale));
-  u.z = __builtin_bit_cast(uint32_t, to_bf16x2(bq.x * scale, bq.y * scale));
-  u.w = __builtin_bit_cast(uint32_t, to_bf16x2(bq.z * scale, bq.w * scale));
-  reinterpret_cast<uint4*>(dq)[i] = u;
-}
+// =====================================================================================
+// dQ
+template <int D>
+struct QCfg {
+  static constexpr int NW = D <= 128 ? 8 : 4;   // waves per workgroup (32 rows each)
+  static constexpr int NT = 64 * NW;
+  static constexpr int BM = 32 * NW;
+  static constexpr int BN = D <= 128 ? 64 : 32;  // keys staged per iteration
+  static constexpr int KSTR = D + 8;             // row-major K / V row stride
+  static constexpr int TSTR = BN + 8;            // K^T row stride
+  static constexpr int SK = BN * KSTR;
+  static constexpr int SKT = D * TSTR;
+  static constexpr int BUF = 2 * SK + SKT;       // K, V, K^T (elements)
+  static constexpr int LDS_BYTES = 2 * BUF * 2;  // double buffered
+};
 
 template <int D>
+__global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    bf16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, int causal, int window, float c,
+    float scale) {
+  using Cfg = QCfg<D>;
+  constexpr int NT = Cfg::NT, BM = Cfg::BM, BN = Cfg::BN, KSTR = Cfg::KSTR, TSTR = Cfg::TSTR;
+  constexpr int NC = D / 16, ND = D / 32;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
+
+  const int num_m = (N + BM - 1) / BM;
+  const int total = B * Hq * num_m;
+  const int lin = xcd_remap(blockIdx.x, total);
+  const int head = lin / num_m;
+  const int mb = num_m - 1 - (lin - head * num_m);
+  const int b = head / Hq, hq = head - b * Hq;
+  const int hkv = hq / (Hq / Hkv);
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int m0 = mb * BM;
+  const int wr0 = m0 + w * 32;
+  const int row = wr0 + l32;
+
+  const size_t qs = (size_t)Hq * D, ks = (size_t)Hkv * D;
+  const bf16_t* Qh = Q + ((size_t)b * N * Hq + hq) * D;
+  const bf16_t* Oh = dO + ((size_t)b * N * Hq + hq) * D;
+  const bf16_t* Kh = K + ((size_t)b * N * Hkv + hkv) * D;
+  const bf16_t* Vh = V + ((size_t)b * N * Hkv + hkv) * D;
+
+  // B operands: this lane's rows of Q and dO.
+  bf16x8 qop[NC], oop[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    qop[cc] = __builtin_bit_cast(bf16x8, row < N ? gload16(Qh + (size_t)row * qs + 16 * cc + 8 * hh) : z);
+    oop[cc] = __builtin_bit_cast(bf16x8, row < N ? gload16(Oh + (size_t)row * qs + 16 * cc + 8 * hh) : z);
+  }
+  const size_t li = ((size_t)b * Hq + hq) * N + row;
+  const float lse2 = row < N ? LSE[li] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
+  const float dval = row < N ? Dv[li] : 0.f;
+
+  int kv_lo = 0, kv_hi = N;
+  if (causal) kv_hi = min(N, m0 + BM);
+  if (window > 0) kv_lo = max(0, m0 - window + 1);
+  const int nb_lo = kv_lo / BN, nb_hi = (kv_hi + BN - 1) / BN;
+  const int klo = window > 0 ? row - window + 1 : 0;  // allowed keys of this row: [klo, khi]
+  const int khi = causal ? min(row, N - 1) : N - 1;
+
+  // Staging tasks: [0, TK) = 4 keys x 8 dims of K (row-major + transposed),
+  // [TK, 2 TK) = the same of V (row-major).
+  constexpr int CPR = D / 8;
+  constexpr int TK = (BN / 4) * CPR;
+  constexpr int PT = (2 * TK + NT - 1) / NT;
+  uint4 xr[PT][4];
+  auto gload = [&](int nb) {
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int task = tid + NT * p;
+      if ((2 * TK) % NT == 0 || task < 2 * TK) {
+        const bool isv = task >= TK;
+        const int t = isv ? task - TK : task;
+        const int kg = t / CPR, dc = t - kg * CPR;
+        load_4x8(xr[p], isv ? Vh : Kh, ks, nb * BN + 4 * kg, N, 8 * dc);
+      }
+    }
+  };
+  auto swrite = [&](int buf) {
+    bf16_t* sK = lds + buf * Cfg::BUF;
+    bf16_t* sV = sK + Cfg::SK;
+    bf16_t* sKT = sV + Cfg::SK;
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int task = tid + NT * p;
+      if ((2 * TK) % NT == 0 || task < 2 * TK) {
+        const bool isv = task >= TK;
+        const int t = isv ? task - TK : task;
+        const int kg = t / CPR, dc = t - kg * CPR;
+        if (isv) {
+          store_4x8_rows(sV, KSTR, 4 * kg, 8 * dc, xr[p]);
+        } else {
+          store_4x8_rows(sK, KSTR, 4 * kg, 8 * dc, xr[p]);
+          store_4x8_transposed(sKT, TSTR, 4 * kg, 8 * dc, xr[p]);
+        }
+      }
+    }
+  };
+
+  f32x16 acc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) acc[i] = zero16();
+
+  if (nb_lo < nb_hi) {
+    gload(nb_lo);
+    swrite(0);
+    if (nb_lo + 1 < nb_hi) gload(nb_lo + 1);
+  }
+  __syncthreads();
+  for (int nb = nb_lo; nb < nb_hi; ++nb) {
+    const int buf = (nb - nb_lo) & 1;
+    const bf16_t* sK = lds + buf * Cfg::BUF;
+    const bf16_t* sV = sK + Cfg::SK;
+    const bf16_t* sKT = sV + Cfg::SK;
+    const int n0 = nb * BN;
+    const bool active = wr0 < N && (!causal || n0 <= wr0 + 31) &&
+                        (window <= 0 || n0 + BN - 1 >= wr0 - window + 1);
+    if (active) {
+#pragma unroll
+      for (int kt = 0; kt < BN / 32; ++kt) {
+        const int k0 = n0 + 32 * kt;
+        if (causal && k0 > wr0 + 31) break;  // piece entirely above the diagonal
+        // S^T = K Q^T and dP^T = V dO^T: keys k0 + [0, 32) x this wave's rows.
+        const bf16_t* kp = sK + (32 * kt + l32) * KSTR + 8 * hh;
+        const bf16_t* vp = sV + (32 * kt + l32) * KSTR + 8 * hh;
+        // Operands are read ahead of their MFMAs when registers allow (d <= 128).
+        constexpr bool kAhead = D <= 128;
+        constexpr int NA = kAhead ? NC : 1;
+        bf16x8 ka[NA], va[NA];
+        if constexpr (kAhead) {
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) {
+            ka[cc] = lds_read_b128(kp + 16 * cc);
+            va[cc] = lds_read_b128(vp + 16 * cc);
+          }
+        }
+        f32x16 s = zero16(), dp = zero16();
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          if constexpr (kAhead) {
+            s = mfma32(ka[cc], qop[cc], s);
+            dp = mfma32(va[cc], oop[cc], dp);
+          } else {
+            s = mfma32(lds_read_b128(kp + 16 * cc), qop[cc], s);
+            dp = mfma32(lds_read_b128(vp + 16 * cc), oop[cc], dp);
+          }
+        }
+        __builtin_amdgcn_s_setprio(0);
+        const bf16_t* tp = sKT + l32 * TSTR + 8 * hh + 32 * kt;
+        constexpr int NTA = kAhead ? ND : 1;
+        bf16x8 ta[NTA][2];
+        if constexpr (kAhead) {
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) ta[dt][c2] = lds_read_b128(tp + 32 * dt * TSTR + 16 * c2);
+        }
+        // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D); masked entries 0.
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[r], c, -lse2));
+        const bool need_mask = (k0 + 32 > N) || (causal && k0 + 31 > wr0) ||
+                               (window > 0 && k0 < wr0 + 32 - window);
+        if (need_mask) {
+          const int kb0 = k0 + hh * 4;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = kb0 + (r >> 2) * 8 + (r & 3);
+            p[r] = ((kk >= klo) & (kk <= khi)) ? p[r] : 0.f;
+          }
+        }
+        bf16x8 pS[2];
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const bf16x2 d2 = to_bf16x2(p[r] * (dp[r] - dval), p[r + 1] * (dp[r + 1] - dval));
+          pS[r >> 3][r & 7] = d2[0];
+          pS[r >> 3][(r & 7) + 1] = d2[1];
+        }
+        // dQ^T += K^T dS^T
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            if constexpr (kAhead)
+              acc[dt] = mfma32(ta[dt][c2], pS[c2], acc[dt]);
+            else
+              acc[dt] = mfma32(lds_read_b128(tp + 32 * dt * TSTR + 16 * c2), pS[c2], acc[dt]);
+          }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    }
+    if (nb + 1 < nb_hi) {
+      swrite(buf ^ 1);
+      if (nb + 2 < nb_hi) gload(nb + 2);
+    }
+    __syncthreads();
+  }
+
+  if (row < N) {
+    bf16_t* qrow = dQ + ((size_t)b * N + row) * qs + (size_t)hq * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        uint2 u;
+        u.x = pack_bf16(acc[dt][4 * g4] * scale, acc[dt][4 * g4 + 1] * scale);
+        u.y = pack_bf16(acc[dt][4 * g4 + 2] * scale, acc[dt][4 * g4 + 3] * scale);
+        *reinterpret_cast<uint2*>(qrow + 32 * dt + 8 * g4 + 4 * hh) = u;
+      }
+    }
+  }
+}
+
+// =====================================================================================
+template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
-  using Cfg = BwdCfg<D>;
+  using KC = KVCfg<D>;
+  using QC = QCfg<D>;
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_bf16_kernel<D>,
+    hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       Cfg::LDS_BYTES);
+                                       KC::LDS_BYTES);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, QC::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done = true;
   }
   const long rows = (long)a.B * a.N * a.Hq;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     st, (const bf16_t*)a.o, (const bf16_t*)a.dO, a.dvec, a.dq_acc, a.B, a.Hq,
-                     a.N);
+                     st, (const bf16_t*)a.o, (const bf16_t*)a.dO, a.dvec, a.B, a.Hq, a.N);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int num_kb = (a.N + Cfg::BKN - 1) / Cfg::BKN;
-  const int grid = a.B * a.Hkv * num_kb * Cfg::NSPLIT;
   if (a.ev_start) {
     e = hipEventRecord(a.ev_start, st);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(bwd_bf16_kernel<D>, dim3(grid), dim3(256), Cfg::LDS_BYTES, st,
-                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
-                     (const bf16_t*)a.dO, a.lse, a.dvec, a.dq_acc, (bf16_t*)a.dk,
-                     (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window,
-                     a.c_log2_signed, a.scale);
+  const int num_kb = (a.N + KC::BKN - 1) / KC::BKN;
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * num_kb * KC::NSPLIT), dim3(KC::NT),
+                     KC::LDS_BYTES, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
+                     (const bf16_t*)a.v, (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dk,
+                     (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window, a.c_log2_signed,
+                     a.scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_stop) {
     e = hipEventRecord(a.ev_stop, st);
     if (e != hipSuccess) return e;
   }
-  const long n8 = rows * D / 8;
-  hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
-                     a.dq_acc, (bf16_t*)a.dq, n8, a.scale);
+  const int num_m = (a.N + QC::BM - 1) / QC::BM;
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.B * a.Hq * num_m), dim3(QC::NT), QC::LDS_BYTES, st,
+                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
+                     (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N,
+                     a.causal, a.window, a.c_log2_signed, a.scale);
   return hipGetLastError();
 }
 

@@ -89,8 +89,71 @@ __device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Max / sum across the two 32-lane halves of a wave (lane l <-> lane l ^ 32).
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Max / sum of a value over the two 32-lane halves of a wave (lanes l and l ^ 32), with
+// one v_permlane32_swap: the two results hold the lower and the upper half in both halves.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Index of the calling wave inside its workgroup, as a scalar (wave-uniform) value.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// ---------------------------------------------------------------------------------
+// Tile staging.  A thread moves a 4-row x 8-column block of a row-major bf16 matrix (4
+// global 16-byte loads) into LDS, either row-major (4 x 16-byte stores) or transposed
+// (8 x 8-byte stores: column j of the block becomes a 4-element run of row j).  In the
+// transposed copy the row index r of a 32-row slab is stored at tpos(r), with bits 2 and 3
+// swapped: an MFMA accumulator holds rows (i / 4) * 8 + h * 4 + i % 4 (i = 0..7) in lane
+// half h, so with this order the 8 rows one lane feeds to a product contracting over rows
+// are contiguous and load as a single 16-byte read.
+__device__ __forceinline__ int tpos(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+__device__ __forceinline__ uint32_t u4word(const uint4& u, int m) {
+  return m == 0 ? u.x : m == 1 ? u.y : m == 2 ? u.z : u.w;
+}
+
+// x[e] = row r0 + e (columns c0 .. c0 + 7); rows at or beyond nrows read as zero.
+__device__ __forceinline__ void load_4x8(uint4 (&x)[4], const bf16_t* base, size_t stride, int r0,
+                                         int nrows, int c0) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    x[e] = r0 + e < nrows ? gload16(base + (size_t)(r0 + e) * stride + c0) : make_uint4(0, 0, 0, 0);
+}
+
+// Row-major store: LDS rows lr0 .. lr0 + 3, row stride s elements.
+__device__ __forceinline__ void store_4x8_rows(bf16_t* lds, int s, int lr0, int c0,
+                                               const uint4 (&x)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) *reinterpret_cast<uint4*>(lds + (lr0 + e) * s + c0) = x[e];
+}
+
+// Transposed store: LDS row c0 + j (j = 0..7) gets the 4 values of column j at positions
+// tpos(lr0) .. tpos(lr0) + 3 (lr0 a multiple of 4), row stride ts elements.
+__device__ __forceinline__ void store_4x8_transposed(bf16_t* lds, int ts, int lr0, int c0,
+                                                     const uint4 (&x)[4]) {
+  bf16_t* dst = lds + c0 * ts + tpos(lr0);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const uint32_t a0 = u4word(x[0], m), a1 = u4word(x[1], m);
+    const uint32_t a2 = u4word(x[2], m), a3 = u4word(x[3], m);
+    uint2 even, odd;  // columns 2m and 2m + 1 of the four rows
+    even.x = (a0 & 0xffffu) | (a1 << 16);
+    even.y = (a2 & 0xffffu) | (a3 << 16);
+    odd.x = (a0 >> 16) | (a1 & 0xffff0000u);
+    odd.y = (a2 >> 16) | (a3 & 0xffff0000u);
+    *reinterpret_cast<uint2*>(dst + (2 * m) * ts) = even;
+    *reinterpret_cast<uint2*>(dst + (2 * m + 1) * ts) = odd;
+  }
+}
 
 // Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).  Map the
 // hardware block id so that consecutive logical ids land on the same XCD: XCD x runs the

@@ -29,29 +29,44 @@ namespace fa {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int BM = 128;      // query rows per workgroup
-  static constexpr int BN = 64;       // keys per iteration
-  static constexpr int STR = D + 8;   // LDS row stride in elements (16-byte pad)
-  static constexpr int LDS_BYTES = 2 * BN * STR * 2;
-  static constexpr int OCC = D <= 128 ? 2 : 1;  // workgroups per CU the registers allow
+  static constexpr int NW = D <= 128 ? 8 : 4;  // waves per workgroup (2 or 1 per SIMD)
+  static constexpr int NT = 64 * NW;           // threads per workgroup
+  static constexpr int BM = 32 * NW;           // query rows per workgroup (32 per wave)
+  static constexpr int BN = D <= 128 ? 64 : 32;  // keys staged per iteration
+  static constexpr int KSTR = D + 8;           // K tile row stride in elements (16-byte pad)
+  static constexpr int VSTR = BN + 8;          // V^T tile row stride in elements (16-byte pad)
+  static constexpr int K_ELEMS = BN * KSTR;
+  static constexpr int V_ELEMS = D * VSTR;
+  static constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
+  static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;  // double buffered
 };
 
-__device__ __forceinline__ bool key_allowed(int row, int key, int N, int causal, int window) {
-  return key < N && (!causal || key <= row) && (window <= 0 || key >= row - window + 1);
+// The running row maximum is only moved when a tile's maximum exceeds it by more than this
+// many log2 units, so probabilities stay below 2^8 and the accumulator rescale (a multiply
+// of every accumulator register) runs rarely.  Numerator and denominator always share the
+// same reference maximum, so the normalised result is unchanged.
+constexpr float kRescaleThreshold = 8.f;
+
+__device__ __forceinline__ uint32_t word(const uint4& u, int m) {
+  return m == 0 ? u.x : m == 1 ? u.y : m == 2 ? u.z : u.w;
 }
 
+// Position of key k (inside a key tile) in the V^T tile: bits 2 and 3 swapped, so that the
+// 8 keys one lane feeds to an MFMA (keys kb + {0..3} and kb + 8 + {0..3}, matching the
+// accumulator layout of S^T) sit next to each other and load as one 16-byte read.
+__device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
 template <int D>
-__global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_bf16_kernel(
+__global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     bf16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N,
     int causal, int window, float c, int neg_q) {
   using Cfg = FwdCfg<D>;
-  constexpr int BM = Cfg::BM, BN = Cfg::BN, STR = Cfg::STR;
+  constexpr int NT = Cfg::NT, BM = Cfg::BM, BN = Cfg::BN, KSTR = Cfg::KSTR, VSTR = Cfg::VSTR;
   constexpr int NC = D / 16;  // k-steps of S^T over the head dim
   constexpr int ND = D / 32;  // 32-wide head-dim tiles of O^T
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16_t* smK = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* smV = smK + BN * STR;
+  bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
 
   const int num_m = (N + BM - 1) / BM;
   const int total = B * Hq * num_m;
@@ -61,9 +76,8 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_bf16_kernel(
   const int b = head / Hq, hq = head - b * Hq;
   const int hkv = hq / (Hq / Hkv);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int hh = lane >> 5, l32 = lane & 31;
-  const int grp = lane >> 4, j16 = lane & 15;
   const int m0 = mb * BM;
   const int wr0 = m0 + w * 32;
   const int row = wr0 + l32;
@@ -93,129 +107,184 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_bf16_kernel(
   if (window > 0) kv_lo = max(0, m0 - window + 1);
   const int nb_lo = kv_lo / BN, nb_hi = (kv_hi + BN - 1) / BN;
 
-  constexpr int CPR = D / 8;          // 16-byte chunks per K/V row
-  constexpr int PT = BN * CPR / 256;  // chunks per thread per tile
-  uint4 kr[PT], vr[PT];
+  // Staging: K rows as 16-byte chunks; V as 4 keys x 8 dims per task, transposed in
+  // registers (16-bit lane packing) and stored as V^T rows.
+  constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
+  constexpr int KCH = BN * CPR;           // K chunks per tile
+  constexpr int PTK = (KCH + NT - 1) / NT;
+  constexpr int VTASKS = (BN / 4) * CPR;  // (4-key group, 8-dim chunk) tasks
+  constexpr int PTV = (VTASKS + NT - 1) / NT;
+  uint4 kr[PTK], vr[PTV][4];
   auto gload = [&](int nb) {
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int ch = tid + 256 * i, key = ch / CPR, dc = ch - key * CPR;
-      const int n = nb * BN + key;
-      if (n < N) {
-        kr[i] = gload16(Kh + (size_t)n * ks + dc * 8);
-        vr[i] = gload16(Vh + (size_t)n * ks + dc * 8);
-      } else {
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < PTK; ++i) {
+      const int ch = tid + NT * i;
+      if (KCH % NT == 0 || ch < KCH) {
+        const int key = ch / CPR, dc = ch - key * CPR;
+        const int n = nb * BN + key;
+        kr[i] = n < N ? gload16(Kh + (size_t)n * ks + dc * 8) : make_uint4(0, 0, 0, 0);
       }
     }
-  };
-  auto swrite = [&]() {
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      const int ch = tid + 256 * i, key = ch / CPR, dc = ch - key * CPR;
-      *reinterpret_cast<uint4*>(smK + key * STR + dc * 8) = kr[i];
-      *reinterpret_cast<uint4*>(smV + key * STR + dc * 8) = vr[i];
-    }
-  };
-
-  float m_i = -INFINITY;  // running max of t (log2 units), shared by both lane halves
-  float l_i = 0.f;        // running sum of this lane's half of the probabilities
-  f32x16 acc[ND];
+    for (int p = 0; p < PTV; ++p) {
+      const int task = tid + NT * p;
+      if (VTASKS % NT == 0 || task < VTASKS) {
+        const int kg = task / CPR, dc = task - kg * CPR;
 #pragma unroll
-  for (int i = 0; i < ND; ++i) acc[i] = zero16();
-
-  if (nb_lo < nb_hi) gload(nb_lo);
-  for (int nb = nb_lo; nb < nb_hi; ++nb) {
-    __syncthreads();
-    swrite();
-    __syncthreads();
-    if (nb + 1 < nb_hi) gload(nb + 1);
-
-    const int n0 = nb * BN;
-    const bool active = wr0 < N && (!causal || n0 <= wr0 + 31) &&
-                        (window <= 0 || n0 + BN - 1 >= wr0 - window + 1);
-    if (!active) continue;
-    const bool need_mask = (n0 + BN > N) || (causal && n0 + BN - 1 > wr0) ||
-                           (window > 0 && n0 < wr0 + 32 - window);
-
-    // S^T tiles for keys n0 + [0, 32) and n0 + [32, 64).
-    f32x16 s0 = zero16(), s1 = zero16();
-    const bf16_t* kp = smK + l32 * STR + 8 * hh;
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const bf16x8 k0 = lds_read_b128(kp + 16 * cc);
-      const bf16x8 k1 = lds_read_b128(kp + 32 * STR + 16 * cc);
-      s0 = mfma32(k0, qop[cc], s0);
-      s1 = mfma32(k1, qop[cc], s1);
-    }
-
-    if (need_mask) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kl = (r >> 2) * 8 + hh * 4 + (r & 3);
-        if (!key_allowed(row, n0 + kl, N, causal, window)) s0[r] = -INFINITY;
-        if (!key_allowed(row, n0 + 32 + kl, N, causal, window)) s1[r] = -INFINITY;
-      }
-    }
-
-    float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = fmaxf(mx, xor32(mx));
-    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-    const float m_new = fmaxf(m_i, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_i - m_use);
-
-    bf16x8 p[2][2];
-    float rs = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      float e0 = fast_exp2(fmaf(s0[r], c, -m_use));
-      float e1 = fast_exp2(fmaf(s0[r + 1], c, -m_use));
-      float f0 = fast_exp2(fmaf(s1[r], c, -m_use));
-      float f1 = fast_exp2(fmaf(s1[r + 1], c, -m_use));
-      if (need_mask) {  // masked entries are exactly 0 (also when scale == 0)
-        if (s0[r] == -INFINITY) e0 = 0.f;
-        if (s0[r + 1] == -INFINITY) e1 = 0.f;
-        if (s1[r] == -INFINITY) f0 = 0.f;
-        if (s1[r + 1] == -INFINITY) f1 = 0.f;
-      }
-      rs += (e0 + e1) + (f0 + f1);
-      const bf16x2 pe = to_bf16x2(e0, e1), pf = to_bf16x2(f0, f1);
-      p[0][r >> 3][r & 7] = pe[0];
-      p[0][r >> 3][(r & 7) + 1] = pe[1];
-      p[1][r >> 3][r & 7] = pf[0];
-      p[1][r >> 3][(r & 7) + 1] = pf[1];
-    }
-    l_i = alpha * l_i + rs;
-    m_i = m_new;
-    if (alpha != 1.f) {
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-    }
-
-    // O^T += V^T P^T : V^T operand via transposed LDS reads.
-    const bf16_t* vbase = smV + (hh * 4 + (j16 >> 2)) * STR + 16 * (grp & 1) + 4 * (j16 & 3);
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2) {
-          const bf16_t* vp = vbase + (kt * 32 + 16 * c2) * STR + 32 * dt;
-          const bf16x8 vop = lds_read_tr_x2(vp, vp + 8 * STR);
-          acc[dt] = mfma32(vop, p[kt][c2], acc[dt]);
+        for (int e = 0; e < 4; ++e) {
+          const int n = nb * BN + 4 * kg + e;
+          vr[p][e] = n < N ? gload16(Vh + (size_t)n * ks + dc * 8) : make_uint4(0, 0, 0, 0);
         }
       }
     }
+  };
+  auto swrite = [&](int buf) {
+    bf16_t* sK = lds + buf * Cfg::BUF_ELEMS;
+    bf16_t* sV = sK + Cfg::K_ELEMS;
+#pragma unroll
+    for (int i = 0; i < PTK; ++i) {
+      const int ch = tid + NT * i;
+      if (KCH % NT == 0 || ch < KCH) {
+        const int key = ch / CPR, dc = ch - key * CPR;
+        *reinterpret_cast<uint4*>(sK + key * KSTR + dc * 8) = kr[i];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PTV; ++p) {
+      const int task = tid + NT * p;
+      if (VTASKS % NT == 0 || task < VTASKS) {
+        const int kg = task / CPR, dc = task - kg * CPR;
+        bf16_t* dst = sV + (dc * 8) * VSTR + vt_pos(4 * kg);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t a0 = word(vr[p][0], m), a1 = word(vr[p][1], m);
+          const uint32_t a2 = word(vr[p][2], m), a3 = word(vr[p][3], m);
+          uint2 even, odd;  // dims 2m and 2m+1, keys 0..3 of the group
+          even.x = (a0 & 0xffffu) | (a1 << 16);
+          even.y = (a2 & 0xffffu) | (a3 << 16);
+          odd.x = (a0 >> 16) | (a1 & 0xffff0000u);
+          odd.y = (a2 >> 16) | (a3 & 0xffff0000u);
+          *reinterpret_cast<uint2*>(dst + (2 * m) * VSTR) = even;
+          *reinterpret_cast<uint2*>(dst + (2 * m + 1) * VSTR) = odd;
+        }
+      }
+    }
+  };
+
+  // Running state of this lane's row: reference max m (log2 units), and this lane-half's
+  // sums of the bf16-rounded weights (normalise O, so O is a convex combination of V rows)
+  // and of the unrounded weights (give the logsumexp).
+  float m_i = -INFINITY, l_i = 0.f, le_i = 0.f;
+  f32x16 acc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) acc[i] = zero16();
+  bf16x2 ones;
+  ones[0] = (__bf16)1.f;
+  ones[1] = (__bf16)1.f;
+  const int klo = window > 0 ? row - window + 1 : 0;  // allowed keys of this row: [klo, khi]
+  const int khi = causal ? min(row, N - 1) : N - 1;
+
+  if (nb_lo < nb_hi) {
+    gload(nb_lo);
+    swrite(0);
+    if (nb_lo + 1 < nb_hi) gload(nb_lo + 1);
+  }
+  __syncthreads();
+  for (int nb = nb_lo; nb < nb_hi; ++nb) {
+    const int buf = (nb - nb_lo) & 1;
+    const bf16_t* sK = lds + buf * Cfg::BUF_ELEMS;
+    const bf16_t* sV = sK + Cfg::K_ELEMS;
+    const int n0 = nb * BN;
+    const bool active = wr0 < N && (!causal || n0 <= wr0 + 31) &&
+                        (window <= 0 || n0 + BN - 1 >= wr0 - window + 1);
+    if (active) {
+      // The staged key tile is processed in 32-key pieces (QK^T, softmax, PV per piece),
+      // which keeps only one 32 x 32 score tile live per wave.
+#pragma unroll
+      for (int kt = 0; kt < BN / 32; ++kt) {
+        const int k0 = n0 + 32 * kt;
+        if (causal && k0 > wr0 + 31) break;  // this half is entirely above the diagonal
+        // S^T tile: keys k0 + [0, 32) x this wave's 32 rows.
+        // All K operands of the piece are read before the MFMAs that use them, and the V^T
+        // operands right after, so LDS latency hides behind the MFMAs and the softmax.
+        const bf16_t* kp = sK + (32 * kt + l32) * KSTR + 8 * hh;
+        bf16x8 kop[NC];
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) kop[cc] = lds_read_b128(kp + 16 * cc);
+        f32x16 s = zero16();
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) s = mfma32(kop[cc], qop[cc], s);
+        const bf16_t* vp = sV + l32 * VSTR + 8 * hh + 32 * kt;
+        bf16x8 vop[ND][2];
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) vop[dt][c2] = lds_read_b128(vp + 32 * dt * VSTR + 16 * c2);
+
+        // Online softmax.  In a piece that crosses the mask band (or the end of the
+        // sequence) the masked scores are first replaced by -inf under a wave-uniform branch;
+        // exp2 of -inf is 0, so the max and exp loops below carry no per-element mask.  The
+        // accumulator rescale sits in one wave-uniform block, so no branch copies it.
+        const bool need_mask = (k0 + 32 > N) || (causal && k0 + 31 > wr0) ||
+                               (window > 0 && k0 < wr0 + 32 - window);
+        if (need_mask) {
+          const int kb0 = k0 + hh * 4;  // key of element r: kb0 + (r / 4) * 8 + r % 4
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb0 + (r >> 2) * 8 + (r & 3);
+            s[r] = ((key >= klo) & (key <= khi)) ? s[r] : -INFINITY;
+          }
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = half_max(mx);
+        const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+        const bool grow = mt > m_i + kRescaleThreshold;
+        if (__any(grow)) {  // wave-uniform: move the reference max of the rows that grew
+          const float alpha = grow ? fast_exp2(m_i - mt) : 1.f;  // 0 when m_i was -inf
+          l_i *= alpha;
+          le_i *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+          m_i = grow ? mt : m_i;
+        }
+        const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
+        bf16x8 pp[2];
+        float rs = 0.f, rse = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float e0 = fast_exp2(fmaf(s[r], c, -m_use));  // exactly 0 for masked scores
+          const float e1 = fast_exp2(fmaf(s[r + 1], c, -m_use));
+          rse += e0 + e1;
+          const bf16x2 pe = to_bf16x2(e0, e1);
+          rs = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rs, false);
+          pp[r >> 3][r & 7] = pe[0];
+          pp[r >> 3][(r & 7) + 1] = pe[1];
+        }
+        l_i += rs;
+        le_i += rse;
+
+        // O^T += V^T P^T.
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) acc[dt] = mfma32(vop[dt][c2], pp[c2], acc[dt]);
+        }
+      }
+    }
+    if (nb + 1 < nb_hi) {
+      swrite(buf ^ 1);
+      if (nb + 2 < nb_hi) gload(nb + 2);
+    }
+    __syncthreads();
   }
 
   // Epilogue: O = acc / l (one rounding to bf16), LSE = (m + log2 l) * ln 2.
-  const float l = l_i + xor32(l_i);
+  const float l = half_sum(l_i);
+  const float le = half_sum(le_i);
   if (row < N) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     bf16_t* orow = O + ((size_t)b * N + row) * qs + (size_t)hq * D;
@@ -232,7 +301,7 @@ __global__ __launch_bounds__(256, FwdCfg<D>::OCC) void fwd_bf16_kernel(
       }
     }
     if (hh == 0)
-      LSE[((size_t)b * Hq + hq) * N + row] = l > 0.f ? (m_i + __log2f(l)) * kLn2 : -INFINITY;
+      LSE[((size_t)b * Hq + hq) * N + row] = le > 0.f ? (m_i + __log2f(le)) * kLn2 : -INFINITY;
   }
 }
 
@@ -345,7 +414,7 @@ static hipError_t launch_fwd_bf16_d(const FwdArgs& a, hipStream_t st) {
   }
   const int num_m = (a.N + Cfg::BM - 1) / Cfg::BM;
   const int grid = a.B * a.Hq * num_m;
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(grid), dim3(256), Cfg::LDS_BYTES, st,
+  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(grid), dim3(Cfg::NT), Cfg::LDS_BYTES, st,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (bf16_t*)a.o,
                      a.lse, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window, a.c_log2, a.neg_q);
   return hipGetLastError();

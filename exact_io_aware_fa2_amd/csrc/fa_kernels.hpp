@@ -31,12 +31,11 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;    // D = rowsum(dO * O), [B, Hq, N]
-  float* dq_acc;  // float32 dQ accumulator, [B, N, Hq, d]
+  float* dvec;  // D = rowsum(dO * O), [B, Hq, N]
   int B, Hq, Hkv, N, d, causal, window;
   float scale;
   float c_log2_signed;  // scale * log2(e)
-  hipEvent_t ev_start;  // optional events recorded around the main kernel (may be null)
+  hipEvent_t ev_start;  // optional events recorded around the key-block kernel (may be null)
   hipEvent_t ev_stop;
 };
 

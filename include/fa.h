@@ -75,10 +75,9 @@ fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, 
                       float scale, void* stream);
 
 /*
- * Bytes of device workspace fa_bwd needs for these sizes.  Linear in N:
- *   [0, a)      D = rowsum(dO * O), float32 [B, Hq, N]             (a = 256-byte aligned)
- *   [a, a + b)  dQ accumulator, float32 [B, N, Hq, d]
- * Returns 0 for arguments fa_bwd would reject.
+ * Bytes of device workspace fa_bwd needs for these sizes: D = rowsum(dO * O) as float32
+ * [B, Hq, N], rounded up to a multiple of 256 bytes.  Linear in N.  Returns 0 for arguments
+ * fa_bwd would reject.
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int window);
 
@@ -91,12 +90,11 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, i
  *   dq [B,N,Hq,d], dk/dv [B,N,Hkv,d] : outputs, bfloat16; dk and dv of a KV head are
  *                    summed over the query heads of its group
  *   workspace      : device buffer of at least fa_bwd_workspace_size(...) bytes, 256-byte
- *                    aligned; its contents on entry are ignored and on return hold D and
- *                    the float32 dQ accumulator (layout above)
- * The pass computes D = rowsum(dO * O), recomputes P = exp(S - lse) block by block, and
- * accumulates dV = P^T dO, dK = scale * dS^T Q with dS = P * (dO V^T - D), dQ = scale * dS K.
- * dQ is accumulated with float32 atomic adds, so its low bits may vary between runs; dK
- * and dV are deterministic.
+ *                    aligned; its contents on entry are ignored and on return hold D
+ * The pass computes D = rowsum(dO * O) from the stored O, then recomputes P = exp(S - lse)
+ * block by block twice: once per key block, accumulating dV = P^T dO and
+ * dK = scale * dS^T Q with dS = P * (dO V^T - D), and once per query block, accumulating
+ * dQ = scale * dS K.  No atomics are used: all outputs are deterministic.
  */
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
@@ -105,9 +103,9 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
 
 /*
  * Benchmark hook (no counterpart on the pages): the next fa_bwd call made on this thread
- * records `start_event` on its stream right before its main recompute kernel and
- * `stop_event` right after it, so a caller can time that kernel alone with
- * hipEventElapsedTime.  Arguments are hipEvent_t handles owned by the caller; passing NULL
+ * records `start_event` on its stream right before its key-block kernel (dK, dV) and
+ * `stop_event` right after it (the query-block kernel for dQ follows), so a caller can time
+ * the backward kernels separately with hipEventElapsedTime.  Arguments are hipEvent_t handles owned by the caller; passing NULL
  * for both clears a pending request.  Returns FA_ERR_INVALID_ARG if exactly one is NULL.
  */
 fa_status fa_bwd_time_main_kernel(void* start_event, void* stop_event);

@@ -94,7 +94,8 @@ def test_backward_validation_and_workspace():
 
 def test_workspace_linear_in_n():
     sizes = [fa.fa_bwd_workspace_size(2, 8, 2, n, 128, 1, 0) for n in (1024, 2048, 4096)]
-    # D (B*Hq*N*4, 256-aligned) + dQ accumulator (B*N*Hq*d*4)
+    # D only: B*Hq*N float32, rounded up to 256 bytes
     for n, s in zip((1024, 2048, 4096), sizes):
-        assert s == ((2 * 8 * n * 4 + 255) // 256) * 256 + 2 * n * 8 * 128 * 4
+        assert s == ((2 * 8 * n * 4 + 255) // 256) * 256
     assert sizes[2] - sizes[1] == 2 * (sizes[1] - sizes[0])
+    assert fa.fa_bwd_workspace_size(1, 1, 1, 3, 64, 0, 0) == 256
