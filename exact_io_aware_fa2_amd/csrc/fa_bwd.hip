@@ -333,6 +333,240 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 }
 
 // =====================================================================================
+// dK / dV for d <= 128: 8 waves x 32 keys = 256 keys per workgroup, two waves per SIMD.
+// Only K stays in VGPRs (B operand of S); V^T for dP is read from an LDS copy of the
+// workgroup's V block, which frees the registers a second wave per SIMD needs, so one
+// wave's exp / dS arithmetic overlaps the other wave's MFMAs.  The Q / dO staging of a
+// 32-row step is shared by all 8 waves.
+template <int D>
+struct KV8Cfg {
+  static constexpr int NW = 8, NT = 512;
+  static constexpr int BKN = 256;         // keys per workgroup
+  static constexpr int BQ = 32;           // query rows per step
+  static constexpr int STR = D + 8;       // row-major V / Q / dO row stride (elements)
+  static constexpr int TSTR = BQ + 8;     // transposed Q^T / dO^T row stride
+  static constexpr int SV = BKN * STR;
+  static constexpr int SQ = BQ * STR;
+  static constexpr int SQT = D * TSTR;
+  static constexpr int BUF = 2 * SQ + 2 * SQT;         // Q, dO, Q^T, dO^T (elements)
+  static constexpr int BUFB = BUF * 2 + 2 * BQ * 4;    // + LSE, D (bytes)
+  static constexpr int LDS_BYTES = SV * 2 + 2 * BUFB;  // V block + double-buffered staging
+};
+
+template <int D>
+__global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
+    int causal, int window, float c, float scale) {
+  using Cfg = KV8Cfg<D>;
+  constexpr int NT = Cfg::NT, BKN = Cfg::BKN, BQ = Cfg::BQ, STR = Cfg::STR, TSTR = Cfg::TSTR;
+  constexpr int NC = D / 16, ND = D / 32;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* sV = reinterpret_cast<bf16_t*>(smem);
+  char* stage = smem + Cfg::SV * 2;
+
+  const int num_kb = (N + BKN - 1) / BKN;
+  const int total = B * Hkv * num_kb;
+  const int lin = xcd_remap(blockIdx.x, total);
+  const int head = lin / num_kb;
+  const int kbo = lin - head * num_kb;
+  const int kb = (!causal && window > 0) ? num_kb - 1 - kbo : kbo;  // longest first
+  const int b = head / Hkv, hkv = head - b * Hkv;
+  const int G = Hq / Hkv;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int n0 = kb * BKN, kw0 = n0 + 32 * w, key = kw0 + l32;
+
+  const size_t qs = (size_t)Hq * D, ks = (size_t)Hkv * D;
+  const bf16_t* Kb = K + ((size_t)b * N * Hkv + hkv) * D;
+  const bf16_t* Vb = V + ((size_t)b * N * Hkv + hkv) * D;
+
+  // K^T B operand of this lane's key; the whole V block into LDS (row-major).
+  bf16x8 kop[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc)
+    kop[cc] = __builtin_bit_cast(
+        bf16x8, key < N ? gload16(Kb + (size_t)key * ks + 16 * cc + 8 * hh) : make_uint4(0, 0, 0, 0));
+  for (int ch = tid; ch < BKN * (D / 8); ch += NT) {
+    const int kl = ch / (D / 8), dc = ch - kl * (D / 8);
+    const int n = n0 + kl;
+    *reinterpret_cast<uint4*>(sV + kl * STR + dc * 8) =
+        n < N ? gload16(Vb + (size_t)n * ks + dc * 8) : make_uint4(0, 0, 0, 0);
+  }
+
+  const int qb_lo = causal ? n0 / BQ : 0;
+  const int row_end = window > 0 ? min(N, n0 + BKN + window - 1) : N;
+  const int qb_hi = (row_end + BQ - 1) / BQ;
+  const int nq = max(0, qb_hi - qb_lo);
+  const int total_it = G * nq;
+
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) {
+    dk[i] = zero16();
+    dv[i] = zero16();
+  }
+
+  // Staging tasks of a step: [0, T1) = 4 rows x 8 dims of Q, [T1, 2 T1) = the same of dO;
+  // each stored row-major and transposed.
+  constexpr int CPR = D / 8;
+  constexpr int T1 = (BQ / 4) * CPR;
+  static_assert(2 * T1 <= NT, "one staging task per thread");
+  uint4 xr[4];
+  float lreg = 0.f, dreg = 0.f;
+  auto gload = [&](int it) {
+    const int g = it / nq, qb = qb_lo + (it - g * nq);
+    const int hq = hkv * G + g, r0 = qb * BQ;
+    if (tid < 2 * T1) {
+      const bool iso = tid >= T1;
+      const int t = iso ? tid - T1 : tid;
+      const int rg = t / CPR, dc = t - rg * CPR;
+      const bf16_t* base = (iso ? dO : Q) + ((size_t)b * N * Hq + hq) * D;
+      load_4x8(xr, base, qs, r0 + 4 * rg, N, 8 * dc);
+    } else if (tid < 2 * T1 + BQ) {
+      const int n = r0 + tid - 2 * T1;
+      const size_t li = ((size_t)b * Hq + hq) * N + n;
+      lreg = n < N ? LSE[li] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
+      dreg = n < N ? Dv[li] : 0.f;
+    }
+  };
+  auto swrite = [&](int buf) {
+    bf16_t* sQ = reinterpret_cast<bf16_t*>(stage + buf * Cfg::BUFB);
+    bf16_t* sO = sQ + Cfg::SQ;
+    bf16_t* sQT = sO + Cfg::SQ;
+    bf16_t* sOT = sQT + Cfg::SQT;
+    float* sL = reinterpret_cast<float*>(sOT + Cfg::SQT);
+    if (tid < 2 * T1) {
+      const bool iso = tid >= T1;
+      const int t = iso ? tid - T1 : tid;
+      const int rg = t / CPR, dc = t - rg * CPR;
+      store_4x8_rows(iso ? sO : sQ, STR, 4 * rg, 8 * dc, xr);
+      store_4x8_transposed(iso ? sOT : sQT, TSTR, 4 * rg, 8 * dc, xr);
+    } else if (tid < 2 * T1 + BQ) {
+      sL[tid - 2 * T1] = lreg;
+      sL[BQ + tid - 2 * T1] = dreg;
+    }
+  };
+
+  if (total_it > 0) {
+    gload(0);
+    swrite(0);
+    if (total_it > 1) gload(1);
+  }
+  __syncthreads();
+  const bf16_t* vp = sV + (32 * w + l32) * STR + 8 * hh;  // V^T B operand rows of this wave
+  for (int it = 0; it < total_it; ++it) {
+    const int buf = it & 1;
+    const bf16_t* sQ = reinterpret_cast<const bf16_t*>(stage + buf * Cfg::BUFB);
+    const bf16_t* sO = sQ + Cfg::SQ;
+    const bf16_t* sQT = sO + Cfg::SQ;
+    const bf16_t* sOT = sQT + Cfg::SQT;
+    const float* sL = reinterpret_cast<const float*>(sOT + Cfg::SQT);
+    const float* sD = sL + BQ;
+    const int g = it / nq, qb = qb_lo + (it - g * nq);
+    const int r0 = qb * BQ;
+    (void)g;
+    const bool active = kw0 < N && (!causal || r0 + BQ - 1 >= kw0) &&
+                        (window <= 0 || r0 <= kw0 + 31 + window - 1);
+    if (active) {
+      // S = Q K^T and dP = dO V^T (lane = key, the step's 32 rows in registers).
+      const bf16_t* qa = sQ + l32 * STR + 8 * hh;
+      const bf16_t* oa = sO + l32 * STR + 8 * hh;
+      f32x16 s = zero16(), dp = zero16();
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        s = mfma32(lds_read_b128(qa + 16 * cc), kop[cc], s);
+        dp = mfma32(lds_read_b128(oa + 16 * cc), lds_read_b128(vp + 16 * cc), dp);
+        // keep the operand reads of later k-steps from being hoisted here: with two waves
+        // per SIMD the other wave covers the LDS latency, and the registers are needed
+        if (cc % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      // P = exp2(S c - LSE log2 e), masked entries 0; dS = P (dP - D).
+      float pv[16];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + 8 * g4 + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pv[4 * g4 + e] = fast_exp2(fmaf(s[4 * g4 + e], c, -L4[e]));
+      }
+      const bool need_mask = (kw0 + 32 > N) || (causal && kw0 + 31 > r0) ||
+                             (window > 0 && kw0 < r0 + BQ - window);
+      if (need_mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = r0 + (r >> 2) * 8 + hh * 4 + (r & 3);
+          const bool ok = (key < N) & (!causal | (key <= row)) &
+                          ((window <= 0) | (key >= row - window + 1));
+          pv[r] = ok ? pv[r] : 0.f;
+        }
+      }
+      bf16x8 pP[2], pS[2];
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 D4 = *reinterpret_cast<const f32x4*>(sD + 8 * g4 + 4 * hh);
+        float dsv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsv[e] = pv[4 * g4 + e] * (dp[4 * g4 + e] - D4[e]);
+        const int c2 = g4 >> 1, i0 = 4 * (g4 & 1);
+        const bf16x2 p01 = to_bf16x2(pv[4 * g4], pv[4 * g4 + 1]);
+        const bf16x2 p23 = to_bf16x2(pv[4 * g4 + 2], pv[4 * g4 + 3]);
+        const bf16x2 d01 = to_bf16x2(dsv[0], dsv[1]), d23 = to_bf16x2(dsv[2], dsv[3]);
+        pP[c2][i0] = p01[0];
+        pP[c2][i0 + 1] = p01[1];
+        pP[c2][i0 + 2] = p23[0];
+        pP[c2][i0 + 3] = p23[1];
+        pS[c2][i0] = d01[0];
+        pS[c2][i0 + 1] = d01[1];
+        pS[c2][i0 + 2] = d23[0];
+        pS[c2][i0 + 3] = d23[1];
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS (A operands from the transposed tiles).
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const bf16_t* ot = sOT + (32 * dt + l32) * TSTR + 8 * hh;
+        const bf16_t* qt = sQT + (32 * dt + l32) * TSTR + 8 * hh;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          dv[dt] = mfma32(lds_read_b128(ot + 16 * c2), pP[c2], dv[dt]);
+          dk[dt] = mfma32(lds_read_b128(qt + 16 * c2), pS[c2], dk[dt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    if (it + 1 < total_it) {
+      swrite(buf ^ 1);
+      if (it + 2 < total_it) gload(it + 2);
+    }
+    __syncthreads();
+  }
+
+  if (key < N) {
+    bf16_t* dkr = dK + ((size_t)b * N + key) * ks + (size_t)hkv * D;
+    bf16_t* dvr = dV + ((size_t)b * N + key) * ks + (size_t)hkv * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * dt + 8 * g4 + 4 * hh;
+        uint2 u;
+        u.x = pack_bf16(dk[dt][4 * g4] * scale, dk[dt][4 * g4 + 1] * scale);
+        u.y = pack_bf16(dk[dt][4 * g4 + 2] * scale, dk[dt][4 * g4 + 3] * scale);
+        *reinterpret_cast<uint2*>(dkr + d) = u;
+        u.x = pack_bf16(dv[dt][4 * g4], dv[dt][4 * g4 + 1]);
+        u.y = pack_bf16(dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3]);
+        *reinterpret_cast<uint2*>(dvr + d) = u;
+      }
+    }
+  }
+}
+
+// =====================================================================================
 // dQ
 template <int D>
 struct QCfg {
@@ -558,12 +792,17 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
 template <int D>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   using KC = KVCfg<D>;
+  using K8 = KV8Cfg<D <= 128 ? D : 128>;
   using QC = QCfg<D>;
+  constexpr bool kWide = D <= 128;  // 8-wave key-block kernel
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       KC::LDS_BYTES);
+    hipError_t e = kWide ? hipFuncSetAttribute((const void*)bwd_dkdv8_kernel<D <= 128 ? D : 128>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               K8::LDS_BYTES)
+                         : hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                                               KC::LDS_BYTES);
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, QC::LDS_BYTES);
@@ -580,12 +819,22 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     e = hipEventRecord(a.ev_start, st);
     if (e != hipSuccess) return e;
   }
-  const int num_kb = (a.N + KC::BKN - 1) / KC::BKN;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * num_kb * KC::NSPLIT), dim3(KC::NT),
-                     KC::LDS_BYTES, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
-                     (const bf16_t*)a.v, (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dk,
-                     (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window, a.c_log2_signed,
-                     a.scale);
+  if constexpr (kWide) {
+    constexpr int DW = D <= 128 ? D : 128;
+    const int num_kb = (a.N + K8::BKN - 1) / K8::BKN;
+    hipLaunchKernelGGL(bwd_dkdv8_kernel<DW>, dim3(a.B * a.Hkv * num_kb), dim3(K8::NT),
+                       K8::LDS_BYTES, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
+                       (const bf16_t*)a.v, (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dk,
+                       (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window,
+                       a.c_log2_signed, a.scale);
+  } else {
+    const int num_kb = (a.N + KC::BKN - 1) / KC::BKN;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * num_kb * KC::NSPLIT),
+                       dim3(KC::NT), KC::LDS_BYTES, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
+                       (const bf16_t*)a.v, (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dk,
+                       (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window,
+                       a.c_log2_signed, a.scale);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_stop) {
