@@ -134,6 +134,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (a known-size kernel "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -251,6 +254,13 @@ def main() -> int:
             "traffic": _traffic(name, w.name, src),
             "avg_launch_ms": ms,
         }
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = src.numel()
+        del src, dst
     out["context"] = ("pages' A100 figures at 16K tokens (other hardware, not a target): "
                       "~50 TFLOP/s standard PyTorch attention vs >180 TFLOP/s FlashAttention-2")
     if not args.no_cpu_baseline:
