@@ -147,6 +147,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // head-dim slice) transposed.
   constexpr int CPR = D / 8;
   constexpr int TASKS = (BQ / 4) * CPR;
+  static_assert(BQ % 16 == 0, "task_rc needs whole groups of 16 rows");
   constexpr int PT = (TASKS + 255) / 256;
   uint4 qr[PT][4], orr[PT][4];
   float lreg = 0.f, dreg = 0.f;
@@ -159,7 +160,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     for (int p = 0; p < PT; ++p) {
       const int task = tid + 256 * p;
       if (TASKS % 256 == 0 || task < TASKS) {
-        const int rg = task / CPR, dc = task - rg * CPR;
+        int rg, dc;
+        task_rc<CPR>(task, rg, dc);
         load_4x8(qr[p], Qb, qs, r0 + 4 * rg, N, 8 * dc);
         load_4x8(orr[p], Ob, qs, r0 + 4 * rg, N, 8 * dc);
       }
@@ -181,7 +183,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     for (int p = 0; p < PT; ++p) {
       const int task = tid + 256 * p;
       if (TASKS % 256 == 0 || task < TASKS) {
-        const int rg = task / CPR, dc = task - rg * CPR;
+        int rg, dc;
+        task_rc<CPR>(task, rg, dc);
         store_4x8_rows(sQ, STR, 4 * rg, 8 * dc, qr[p]);
         store_4x8_rows(sO, STR, 4 * rg, 8 * dc, orr[p]);
         const int dl = 8 * dc - dh0;
@@ -413,6 +416,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   // each stored row-major and transposed.
   constexpr int CPR = D / 8;
   constexpr int T1 = (BQ / 4) * CPR;
+  static_assert(BQ % 16 == 0, "task_rc needs whole groups of 16 rows");
   static_assert(2 * T1 <= NT, "one staging task per thread");
   uint4 xr[4];
   float lreg = 0.f, dreg = 0.f;
@@ -422,7 +426,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     if (tid < 2 * T1) {
       const bool iso = tid >= T1;
       const int t = iso ? tid - T1 : tid;
-      const int rg = t / CPR, dc = t - rg * CPR;
+      int rg, dc;
+      task_rc<CPR>(t, rg, dc);
       const bf16_t* base = (iso ? dO : Q) + ((size_t)b * N * Hq + hq) * D;
       load_4x8(xr, base, qs, r0 + 4 * rg, N, 8 * dc);
     } else if (tid < 2 * T1 + BQ) {
@@ -441,7 +446,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     if (tid < 2 * T1) {
       const bool iso = tid >= T1;
       const int t = iso ? tid - T1 : tid;
-      const int rg = t / CPR, dc = t - rg * CPR;
+      int rg, dc;
+      task_rc<CPR>(t, rg, dc);
       store_4x8_rows(iso ? sO : sQ, STR, 4 * rg, 8 * dc, xr);
       store_4x8_transposed(iso ? sOT : sQT, TSTR, 4 * rg, 8 * dc, xr);
     } else if (tid < 2 * T1 + BQ) {
@@ -637,6 +643,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   // [TK, 2 TK) = the same of V (row-major).
   constexpr int CPR = D / 8;
   constexpr int TK = (BN / 4) * CPR;
+  static_assert(BN % 16 == 0, "task_rc needs whole groups of 16 rows");
   constexpr int PT = (2 * TK + NT - 1) / NT;
   uint4 xr[PT][4];
   auto gload = [&](int nb) {
@@ -646,7 +653,8 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
       if ((2 * TK) % NT == 0 || task < 2 * TK) {
         const bool isv = task >= TK;
         const int t = isv ? task - TK : task;
-        const int kg = t / CPR, dc = t - kg * CPR;
+        int kg, dc;
+        task_rc<CPR>(t, kg, dc);
         load_4x8(xr[p], isv ? Vh : Kh, ks, nb * BN + 4 * kg, N, 8 * dc);
       }
     }
@@ -661,7 +669,8 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
       if ((2 * TK) % NT == 0 || task < 2 * TK) {
         const bool isv = task >= TK;
         const int t = isv ? task - TK : task;
-        const int kg = t / CPR, dc = t - kg * CPR;
+        int kg, dc;
+        task_rc<CPR>(t, kg, dc);
         if (isv) {
           store_4x8_rows(sV, KSTR, 4 * kg, 8 * dc, xr[p]);
         } else {

@@ -121,6 +121,19 @@ __device__ __forceinline__ uint32_t u4word(const uint4& u, int m) {
   return m == 0 ? u.x : m == 1 ? u.y : m == 2 ? u.z : u.w;
 }
 
+// Order of the (4-row group, 8-column chunk) staging tasks.  Four neighbouring lanes take
+// four consecutive row groups of one column chunk, the next four lanes the next chunk:
+// the 8-byte transposed stores of any 8 lanes then hit 64 distinct banks, and so do the
+// 16-byte row-major stores (the plain group-major order leaves the transposed stores
+// 4-way conflicted).  A wave still reads rows of up to 256 contiguous bytes from memory.
+// A bijection on [0, (rows / 4) * CPR) when rows is a multiple of 16.
+template <int CPR>
+__device__ __forceinline__ void task_rc(int t, int& rg, int& dc) {
+  const int q = t >> 2;
+  dc = q % CPR;
+  rg = (q / CPR) * 4 + (t & 3);
+}
+
 // x[e] = row r0 + e (columns c0 .. c0 + 7); rows at or beyond nrows read as zero.
 __device__ __forceinline__ void load_4x8(uint4 (&x)[4], const bf16_t* base, size_t stride, int r0,
                                          int nrows, int c0) {

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   constexpr int KCH = BN * CPR;           // K chunks per tile
   constexpr int PTK = (KCH + NT - 1) / NT;
   constexpr int VTASKS = (BN / 4) * CPR;  // (4-key group, 8-dim chunk) tasks
+  static_assert(BN % 16 == 0, "task_rc needs whole groups of 16 keys");
   constexpr int PTV = (VTASKS + NT - 1) / NT;
   uint4 kr[PTK], vr[PTV][4];
   auto gload = [&](int nb) {
@@ -129,7 +130,8 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
     for (int p = 0; p < PTV; ++p) {
       const int task = tid + NT * p;
       if (VTASKS % NT == 0 || task < VTASKS) {
-        const int kg = task / CPR, dc = task - kg * CPR;
+        int kg, dc;
+        task_rc<CPR>(task, kg, dc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int n = nb * BN + 4 * kg + e;
@@ -153,7 +155,8 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
     for (int p = 0; p < PTV; ++p) {
       const int task = tid + NT * p;
       if (VTASKS % NT == 0 || task < VTASKS) {
-        const int kg = task / CPR, dc = task - kg * CPR;
+        int kg, dc;
+        task_rc<CPR>(task, kg, dc);
         bf16_t* dst = sV + (dc * 8) * VSTR + vt_pos(4 * kg);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -212,8 +215,12 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) kop[cc] = lds_read_b128(kp + 16 * cc);
         f32x16 s = zero16();
+        // Raised wave priority over each MFMA run: the other wave on the SIMD gets the
+        // softmax VALU slots while this one keeps the matrix core fed.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) s = mfma32(kop[cc], qop[cc], s);
+        __builtin_amdgcn_s_setprio(0);
         const bf16_t* vp = sV + l32 * VSTR + 8 * hh + 32 * kt;
         bf16x8 vop[ND][2];
 #pragma unroll
@@ -268,11 +275,13 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
         le_i += rse;
 
         // O^T += V^T P^T.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int dt = 0; dt < ND; ++dt) {
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) acc[dt] = mfma32(vop[dt][c2], pp[c2], acc[dt]);
         }
+        __builtin_amdgcn_s_setprio(0);
       }
     }
     if (nb + 1 < nb_hi) {
