@@ -86,10 +86,9 @@ def cpu_baseline(w, q, k, v, do, max_workers: int = 16):
     workers = max(1, min(max_workers, cores))
     per_head_f = fwd_flops(w) / (w.B * w.Hq)
     bwd = do is not None
-    # about 10-30 s of work: ~3 heads per worker at the headline size, fewer if larger
-    est_head_s = per_head_f * (3.5 if bwd else 1.0) / 15e9
-    per_worker = max(1, min(4, int(12.0 / max(est_head_s, 1e-3))))
-    n_heads = min(w.B * w.Hq, workers * per_worker)
+    # about 20 s of wall time at ~25 GFLOP/s per float64 worker, at most the whole workload
+    est_head_s = per_head_f * (3.5 if bwd else 1.0) / 25e9
+    n_heads = min(w.B * w.Hq, max(workers, int(20.0 * workers / max(est_head_s, 1e-3))))
     g = w.Hq // w.Hkv
     pairs = [(i // w.Hq, i % w.Hq) for i in range(n_heads)]
     f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
@@ -238,7 +237,9 @@ def main() -> int:
         out["fwd_bwd_frac_of_peak"] = out["value"] / MFMA_BF16_PEAK_TFLOPS
         # algorithmic products executed by each kernel: dK/dV kernel S, dP, dV, dK (4 per
         # pair, 2x the forward); dQ kernel S, dP, dQ (3 per pair, 1.5x the forward)
-        kernels["bwd_dkdv_kernel"] = (avg(kv_ms), 2.0 * F, "fa_bwd.hip")
+        # d <= 128 runs the 8-wave key-block kernel, d = 256 the 4-wave one
+        kv_name = "bwd_dkdv8_kernel" if w.d <= 128 else "bwd_dkdv_kernel"
+        kernels[kv_name] = (avg(kv_ms), 2.0 * F, "fa_bwd.hip")
         kernels["bwd_dq_kernel"] = (avg(q_ms), 1.5 * F, "fa_bwd.hip")
     if w.dtype == "bf16":
         name = max(kernels, key=lambda n: kernels[n][0])

@@ -156,14 +156,18 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const int hq = hkv * G + g, r0 = qb * BQ;
     const bf16_t* Qb = Q + ((size_t)b * N * Hq + hq) * D;
     const bf16_t* Ob = dO + ((size_t)b * N * Hq + hq) * D;
+    const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
+    const rsrc_t qres = make_rsrc(Qb + (size_t)r0 * qs, bytes);
+    const rsrc_t ores = make_rsrc(Ob + (size_t)r0 * qs, bytes);
 #pragma unroll
     for (int p = 0; p < PT; ++p) {
       const int task = tid + 256 * p;
       if (TASKS % 256 == 0 || task < TASKS) {
         int rg, dc;
         task_rc<CPR>(task, rg, dc);
-        load_4x8(qr[p], Qb, qs, r0 + 4 * rg, N, 8 * dc);
-        load_4x8(orr[p], Ob, qs, r0 + 4 * rg, N, 8 * dc);
+        const uint32_t off = (uint32_t)(4 * rg * qs + 8 * dc) * 2u;
+        bload_4x8(qr[p], qres, off, (uint32_t)qs * 2u);
+        bload_4x8(orr[p], ores, off, (uint32_t)qs * 2u);
       }
     }
     if (tid < BQ) {
@@ -418,18 +422,22 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   constexpr int T1 = (BQ / 4) * CPR;
   static_assert(BQ % 16 == 0, "task_rc needs whole groups of 16 rows");
   static_assert(2 * T1 <= NT, "one staging task per thread");
+  static_assert(T1 % 64 == 0, "Q and dO tasks fall on whole waves");
+  // Which operand a wave stages is wave-uniform, so its buffer resource stays scalar.
+  const bool stager = w < 2 * T1 / 64, iso = w >= T1 / 64;
   uint4 xr[4];
   float lreg = 0.f, dreg = 0.f;
   auto gload = [&](int it) {
     const int g = it / nq, qb = qb_lo + (it - g * nq);
     const int hq = hkv * G + g, r0 = qb * BQ;
-    if (tid < 2 * T1) {
-      const bool iso = tid >= T1;
+    if (stager) {
       const int t = iso ? tid - T1 : tid;
       int rg, dc;
       task_rc<CPR>(t, rg, dc);
-      const bf16_t* base = (iso ? dO : Q) + ((size_t)b * N * Hq + hq) * D;
-      load_4x8(xr, base, qs, r0 + 4 * rg, N, 8 * dc);
+      const bf16_t* base = (iso ? dO : Q) + ((size_t)b * N * Hq + hq) * D + (size_t)r0 * qs;
+      const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
+      bload_4x8(xr, make_rsrc(base, bytes), (uint32_t)(4 * rg * qs + 8 * dc) * 2u,
+                (uint32_t)qs * 2u);
     } else if (tid < 2 * T1 + BQ) {
       const int n = r0 + tid - 2 * T1;
       const size_t li = ((size_t)b * Hq + hq) * N + n;
@@ -443,8 +451,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     bf16_t* sQT = sO + Cfg::SQ;
     bf16_t* sOT = sQT + Cfg::SQT;
     float* sL = reinterpret_cast<float*>(sOT + Cfg::SQT);
-    if (tid < 2 * T1) {
-      const bool iso = tid >= T1;
+    if (stager) {
       const int t = iso ? tid - T1 : tid;
       int rg, dc;
       task_rc<CPR>(t, rg, dc);
@@ -645,17 +652,21 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   constexpr int TK = (BN / 4) * CPR;
   static_assert(BN % 16 == 0, "task_rc needs whole groups of 16 rows");
   constexpr int PT = (2 * TK + NT - 1) / NT;
+  static_assert(TK % 64 == 0, "K and V tasks fall on whole waves");
   uint4 xr[PT][4];
   auto gload = [&](int nb) {
 #pragma unroll
     for (int p = 0; p < PT; ++p) {
       const int task = tid + NT * p;
-      if ((2 * TK) % NT == 0 || task < 2 * TK) {
-        const bool isv = task >= TK;
+      const int wtask = 64 * w + NT * p;  // first task of this wave: wave-uniform
+      if ((2 * TK) % NT == 0 || wtask < 2 * TK) {
+        const bool isv = wtask >= TK;  // wave-uniform, keeps the buffer resource scalar
         const int t = isv ? task - TK : task;
         int kg, dc;
         task_rc<CPR>(t, kg, dc);
-        load_4x8(xr[p], isv ? Vh : Kh, ks, nb * BN + 4 * kg, N, 8 * dc);
+        const uint32_t bytes = (uint32_t)(N - nb * BN) * (uint32_t)ks * 2u;  // rows past N read 0
+        const rsrc_t res = make_rsrc((isv ? Vh : Kh) + (size_t)nb * BN * ks, bytes);
+        bload_4x8(xr[p], res, (uint32_t)(4 * kg * ks + 8 * dc) * 2u, (uint32_t)ks * 2u);
       }
     }
   };

@@ -69,6 +69,30 @@ __device__ __forceinline__ uint4 gload16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Raw buffer loads.  A buffer resource covers `bytes` bytes from `base`; a 16-byte load at
+// an offset at or beyond that size returns zeros instead of touching memory, which pads a
+// partial tile without per-lane tests.  The third descriptor dword selects the 32-bit data
+// format that untyped buffer loads on this chip family expect.
+constexpr int kBufferDword3 = 0x00020000;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferDword3);
+}
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+
+// Low (sel_lo) or high (sel_hi) 16-bit halves of two words packed into one word:
+// pack_lo(a, b) = a[15:0] | b[15:0] << 16, pack_hi(a, b) = a[31:16] | b[31:16] << 16.
+// One v_perm_b32 each (its second source supplies bytes 0-3, its first bytes 4-7).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
 // Flip the sign bit of 8 packed bfloat16 values (exact negation).
 __device__ __forceinline__ bf16x8 negate8(const bf16x8& x) {
   uint4 u = __builtin_bit_cast(uint4, x);
@@ -134,12 +158,12 @@ __device__ __forceinline__ void task_rc(int t, int& rg, int& dc) {
   rg = (q / CPR) * 4 + (t & 3);
 }
 
-// x[e] = row r0 + e (columns c0 .. c0 + 7); rows at or beyond nrows read as zero.
-__device__ __forceinline__ void load_4x8(uint4 (&x)[4], const bf16_t* base, size_t stride, int r0,
-                                         int nrows, int c0) {
+// x[e] = 16 bytes at byte offset off + e * row_bytes of a buffer resource (zeros past its
+// end): row e of a 4 x 8 block when off addresses its first row.
+__device__ __forceinline__ void bload_4x8(uint4 (&x)[4], rsrc_t res, uint32_t off,
+                                          uint32_t row_bytes) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    x[e] = r0 + e < nrows ? gload16(base + (size_t)(r0 + e) * stride + c0) : make_uint4(0, 0, 0, 0);
+  for (int e = 0; e < 4; ++e) x[e] = bload16(res, off + e * row_bytes);
 }
 
 // Row-major store: LDS rows lr0 .. lr0 + 3, row stride s elements.
@@ -159,10 +183,10 @@ __device__ __forceinline__ void store_4x8_transposed(bf16_t* lds, int ts, int lr
     const uint32_t a0 = u4word(x[0], m), a1 = u4word(x[1], m);
     const uint32_t a2 = u4word(x[2], m), a3 = u4word(x[3], m);
     uint2 even, odd;  // columns 2m and 2m + 1 of the four rows
-    even.x = (a0 & 0xffffu) | (a1 << 16);
-    even.y = (a2 & 0xffffu) | (a3 << 16);
-    odd.x = (a0 >> 16) | (a1 & 0xffff0000u);
-    odd.y = (a2 >> 16) | (a3 & 0xffff0000u);
+    even.x = pack_lo(a0, a1);
+    even.y = pack_lo(a2, a3);
+    odd.x = pack_hi(a0, a1);
+    odd.y = pack_hi(a2, a3);
     *reinterpret_cast<uint2*>(dst + (2 * m) * ts) = even;
     *reinterpret_cast<uint2*>(dst + (2 * m + 1) * ts) = odd;
   }

@@ -115,28 +115,37 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   constexpr int VTASKS = (BN / 4) * CPR;  // (4-key group, 8-dim chunk) tasks
   static_assert(BN % 16 == 0, "task_rc needs whole groups of 16 keys");
   constexpr int PTV = (VTASKS + NT - 1) / NT;
+  // Tiles are read through buffer resources whose size ends at row N, so rows past the end
+  // of the sequence load as zeros; the per-thread byte offsets inside a tile are fixed.
   uint4 kr[PTK], vr[PTV][4];
+  uint32_t koff[PTK], voff[PTV];
+#pragma unroll
+  for (int i = 0; i < PTK; ++i) {
+    const int ch = tid + NT * i;
+    const int key = ch / CPR, dc = ch - key * CPR;
+    koff[i] = (uint32_t)(key * ks + dc * 8) * 2u;
+  }
+#pragma unroll
+  for (int p = 0; p < PTV; ++p) {
+    int kg, dc;
+    task_rc<CPR>(tid + NT * p, kg, dc);
+    voff[p] = (uint32_t)(4 * kg * ks + dc * 8) * 2u;
+  }
+  const uint32_t row_bytes = (uint32_t)ks * 2u;
   auto gload = [&](int nb) {
+    const int n0 = nb * BN;
+    const uint32_t bytes = (uint32_t)(N - n0) * row_bytes;
+    const rsrc_t kres = make_rsrc(Kh + (size_t)n0 * ks, bytes);
+    const rsrc_t vres = make_rsrc(Vh + (size_t)n0 * ks, bytes);
 #pragma unroll
     for (int i = 0; i < PTK; ++i) {
-      const int ch = tid + NT * i;
-      if (KCH % NT == 0 || ch < KCH) {
-        const int key = ch / CPR, dc = ch - key * CPR;
-        const int n = nb * BN + key;
-        kr[i] = n < N ? gload16(Kh + (size_t)n * ks + dc * 8) : make_uint4(0, 0, 0, 0);
-      }
+      if (KCH % NT == 0 || tid + NT * i < KCH) kr[i] = bload16(kres, koff[i]);
     }
 #pragma unroll
     for (int p = 0; p < PTV; ++p) {
-      const int task = tid + NT * p;
-      if (VTASKS % NT == 0 || task < VTASKS) {
-        int kg, dc;
-        task_rc<CPR>(task, kg, dc);
+      if (VTASKS % NT == 0 || tid + NT * p < VTASKS) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int n = nb * BN + 4 * kg + e;
-          vr[p][e] = n < N ? gload16(Vh + (size_t)n * ks + dc * 8) : make_uint4(0, 0, 0, 0);
-        }
+        for (int e = 0; e < 4; ++e) vr[p][e] = bload16(vres, voff[p] + e * row_bytes);
       }
     }
   };
@@ -163,10 +172,10 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
           const uint32_t a0 = word(vr[p][0], m), a1 = word(vr[p][1], m);
           const uint32_t a2 = word(vr[p][2], m), a3 = word(vr[p][3], m);
           uint2 even, odd;  // dims 2m and 2m+1, keys 0..3 of the group
-          even.x = (a0 & 0xffffu) | (a1 << 16);
-          even.y = (a2 & 0xffffu) | (a3 << 16);
-          odd.x = (a0 >> 16) | (a1 & 0xffff0000u);
-          odd.y = (a2 >> 16) | (a3 & 0xffff0000u);
+          even.x = pack_lo(a0, a1);
+          even.y = pack_lo(a2, a3);
+          odd.x = pack_hi(a0, a1);
+          odd.y = pack_hi(a2, a3);
           *reinterpret_cast<uint2*>(dst + (2 * m) * VSTR) = even;
           *reinterpret_cast<uint2*>(dst + (2 * m + 1) * VSTR) = odd;
         }
@@ -242,9 +251,9 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
             s[r] = ((key >= klo) & (key <= khi)) ? s[r] : -INFINITY;
           }
         }
-        float mx = s[0];
+        float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);  // v_max3
         mx = half_max(mx);
         const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
         const bool grow = mt > m_i + kRescaleThreshold;
