@@ -425,11 +425,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   static_assert(T1 % 64 == 0, "Q and dO tasks fall on whole waves");
   // Which operand a wave stages is wave-uniform, so its buffer resource stays scalar.
   const bool stager = w < 2 * T1 / 64, iso = w >= T1 / 64;
+  // Every thread fetches the LSE / D value of row tid % BQ of the step, unconditionally and
+  // unscaled: a load consumed only at the next step's LDS write must not sit on a branch
+  // merge or feed arithmetic right away, or the wait for it lands right behind its issue.
   uint4 xr[4];
-  float lreg = 0.f, dreg = 0.f;
+  float lraw = 0.f, draw = 0.f;
+  auto step_r0 = [&](int it) { return (qb_lo + it % nq) * BQ; };
   auto gload = [&](int it) {
-    const int g = it / nq, qb = qb_lo + (it - g * nq);
-    const int hq = hkv * G + g, r0 = qb * BQ;
+    const int g = it / nq, hq = hkv * G + g, r0 = step_r0(it);
     if (stager) {
       const int t = iso ? tid - T1 : tid;
       int rg, dc;
@@ -438,14 +441,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
       bload_4x8(xr, make_rsrc(base, bytes), (uint32_t)(4 * rg * qs + 8 * dc) * 2u,
                 (uint32_t)qs * 2u);
-    } else if (tid < 2 * T1 + BQ) {
-      const int n = r0 + tid - 2 * T1;
-      const size_t li = ((size_t)b * Hq + hq) * N + n;
-      lreg = n < N ? LSE[li] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
-      dreg = n < N ? Dv[li] : 0.f;
     }
+    const size_t l0 = ((size_t)b * Hq + hq) * N + r0;
+    const uint32_t lbytes = (uint32_t)(N - r0) * 4u;
+    const uint32_t loff = (uint32_t)(tid % BQ) * 4u;
+    lraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        make_rsrc(LSE + l0, lbytes), (int)loff, 0, 0));
+    draw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        make_rsrc(Dv + l0, lbytes), (int)loff, 0, 0));
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf, int it) {
     bf16_t* sQ = reinterpret_cast<bf16_t*>(stage + buf * Cfg::BUFB);
     bf16_t* sO = sQ + Cfg::SQ;
     bf16_t* sQT = sO + Cfg::SQ;
@@ -457,15 +462,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       task_rc<CPR>(t, rg, dc);
       store_4x8_rows(iso ? sO : sQ, STR, 4 * rg, 8 * dc, xr);
       store_4x8_transposed(iso ? sOT : sQT, TSTR, 4 * rg, 8 * dc, xr);
-    } else if (tid < 2 * T1 + BQ) {
-      sL[tid - 2 * T1] = lreg;
-      sL[BQ + tid - 2 * T1] = dreg;
+    }
+    if (tid < BQ) {
+      const bool in = step_r0(it) + tid < N;
+      sL[tid] = in ? lraw * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
+      sL[BQ + tid] = in ? draw : 0.f;
     }
   };
 
   if (total_it > 0) {
     gload(0);
-    swrite(0);
+    swrite(0, 0);
     if (total_it > 1) gload(1);
   }
   __syncthreads();
@@ -553,7 +560,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       __builtin_amdgcn_s_setprio(0);
     }
     if (it + 1 < total_it) {
-      swrite(buf ^ 1);
+      swrite(buf ^ 1, it + 1);
       if (it + 2 < total_it) gload(it + 2);
     }
     __syncthreads();
