@@ -41,11 +41,15 @@ struct FwdCfg {
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;  // double buffered
 };
 
-// The running row maximum is only moved when a tile's maximum exceeds it by more than this
-// many log2 units, so probabilities stay below 2^8 and the accumulator rescale (a multiply
-// of every accumulator register) runs rarely.  Numerator and denominator always share the
-// same reference maximum, so the normalised result is unchanged.
+// Lazy reference maximum.  A piece whose weights against the current reference would
+// exceed kSumLimit = 2^12 (detected from a lane's partial sum, so the common path takes no
+// row max at all) goes through the rescale path, which moves the reference only for rows
+// whose piece maximum exceeds it by more than kRescaleThreshold log2 units.  Weights thus
+// stay below 2^12 and the accumulator rescale (a multiply of every accumulator register)
+// runs rarely.  Numerator and denominator always share the same reference maximum, so the
+// normalised result is unchanged.
 constexpr float kRescaleThreshold = 8.f;
+constexpr float kSumLimit = 4096.f;
 
 __device__ __forceinline__ uint32_t word(const uint4& u, int m) {
   return m == 0 ? u.x : m == 1 ? u.y : m == 2 ? u.z : u.w;
@@ -251,13 +255,25 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
             s[r] = ((key >= klo) & (key <= khi)) ? s[r] : -INFINITY;
           }
         }
-        float mx = fmaxf(s[0], s[1]);
+        // Weights against the current reference max first.  The row max of the piece is
+        // only taken, and the reference moved, when that cannot stand: a lane's partial sum
+        // above kSumLimit (a weight above it, or overflow) or no reference yet (the sum is
+        // then inf or NaN).  Otherwise weights stay below 2^12 and no max is needed.
+        float e[16];
+        float rse = 0.f;
 #pragma unroll
-        for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);  // v_max3
-        mx = half_max(mx);
-        const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-        const bool grow = mt > m_i + kRescaleThreshold;
-        if (__any(grow)) {  // wave-uniform: move the reference max of the rows that grew
+        for (int r = 0; r < 16; r += 2) {
+          e[r] = fast_exp2(fmaf(s[r], c, -m_i));  // exactly 0 for masked scores
+          e[r + 1] = fast_exp2(fmaf(s[r + 1], c, -m_i));
+          rse += e[r] + e[r + 1];
+        }
+        if (__any(!(rse <= kSumLimit))) {  // wave-uniform; rare after a row's first piece
+          float mx = fmaxf(s[0], s[1]);
+#pragma unroll
+          for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);  // v_max3
+          mx = half_max(mx);
+          const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+          const bool grow = mt > m_i + kRescaleThreshold;
           const float alpha = grow ? fast_exp2(m_i - mt) : 1.f;  // 0 when m_i was -inf
           l_i *= alpha;
           le_i *= alpha;
@@ -266,16 +282,20 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
           m_i = grow ? mt : m_i;
+          const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
+          rse = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            e[r] = fast_exp2(fmaf(s[r], c, -m_use));
+            e[r + 1] = fast_exp2(fmaf(s[r + 1], c, -m_use));
+            rse += e[r] + e[r + 1];
+          }
         }
-        const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
         bf16x8 pp[2];
-        float rs = 0.f, rse = 0.f;
+        float rs = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float e0 = fast_exp2(fmaf(s[r], c, -m_use));  // exactly 0 for masked scores
-          const float e1 = fast_exp2(fmaf(s[r + 1], c, -m_use));
-          rse += e0 + e1;
-          const bf16x2 pe = to_bf16x2(e0, e1);
+          const bf16x2 pe = to_bf16x2(e[r], e[r + 1]);
           rs = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rs, false);
           pp[r >> 3][r & 7] = pe[0];
           pp[r >> 3][(r & 7) + 1] = pe[1];
