@@ -50,9 +50,12 @@ def fwd_flops(w) -> float:
 
 
 def _src_sha(name: str) -> str:
-    p = os.path.join(ROOT, "exact_io_aware_fa2_amd", "csrc", name)
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source together with the headers every kernel source includes."""
+    h = hashlib.sha256()
+    for n in (name, "fa_common.hpp", "fa_kernels.hpp"):
+        with open(os.path.join(ROOT, "exact_io_aware_fa2_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _traffic(kernel: str, workload: str, source: str):
