@@ -259,14 +259,18 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
         // only taken, and the reference moved, when that cannot stand: a lane's partial sum
         // above kSumLimit (a weight above it, or overflow) or no reference yet (the sum is
         // then inf or NaN).  Otherwise weights stay below 2^12 and no max is needed.
-        float e[16];
-        float rse = 0.f;
+        // Sums are taken as trees, not serial chains, so the wave's VALU work stays
+        // independent enough to issue back to back.
+        auto tree_sum = [](const float (&x)[16]) {
+          float q[8];
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          e[r] = fast_exp2(fmaf(s[r], c, -m_i));  // exactly 0 for masked scores
-          e[r + 1] = fast_exp2(fmaf(s[r + 1], c, -m_i));
-          rse += e[r] + e[r + 1];
-        }
+          for (int i = 0; i < 8; ++i) q[i] = x[2 * i] + x[2 * i + 1];
+          return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+        };
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(s[r], c, -m_i));  // 0 if masked
+        float rse = tree_sum(e);
         if (__any(!(rse <= kSumLimit))) {  // wave-uniform; rare after a row's first piece
           float mx = fmaxf(s[0], s[1]);
 #pragma unroll
@@ -283,23 +287,20 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
             for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
           m_i = grow ? mt : m_i;
           const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
-          rse = 0.f;
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            e[r] = fast_exp2(fmaf(s[r], c, -m_use));
-            e[r + 1] = fast_exp2(fmaf(s[r + 1], c, -m_use));
-            rse += e[r] + e[r + 1];
-          }
+          for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(s[r], c, -m_use));
+          rse = tree_sum(e);
         }
         bf16x8 pp[2];
-        float rs = 0.f;
+        float rs2[2] = {0.f, 0.f};  // two dot chains, one per half of the piece
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const bf16x2 pe = to_bf16x2(e[r], e[r + 1]);
-          rs = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rs, false);
+          rs2[r >> 3] = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rs2[r >> 3], false);
           pp[r >> 3][r & 7] = pe[0];
           pp[r >> 3][(r & 7) + 1] = pe[1];
         }
+        const float rs = rs2[0] + rs2[1];
         l_i += rs;
         le_i += rse;
 
