@@ -50,9 +50,9 @@ def fwd_flops(w) -> float:
 
 
 def _src_sha(name: str) -> str:
-    """Hash of a kernel source together with the headers every kernel source includes."""
+    """Hash of a kernel source together with the device-code header every kernel includes."""
     h = hashlib.sha256()
-    for n in (name, "fa_common.hpp", "fa_kernels.hpp"):
+    for n in (name, "fa_common.hpp"):
         with open(os.path.join(ROOT, "exact_io_aware_fa2_amd", "csrc", n), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -72,6 +72,26 @@ def _traffic(kernel: str, workload: str, source: str):
     if not rec or rec.get("source_sha") != _src_sha(source):
         return None
     return rec.get("bytes_per_launch")
+
+
+def mfma_probe(fa, torch, dev, stream, blocks: int = 2048, iters: int = 20000, reps: int = 3):
+    """Sustained bf16 MFMA throughput of a products-only kernel (TFLOP/s, best of reps)."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    sh = stream.cuda_stream
+    if fa.fa_mfma_probe(out, blocks, 100, sh) != fa.FA_OK:
+        raise RuntimeError(fa.fa_last_error())
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if fa.fa_mfma_probe(out, blocks, iters, sh) != fa.FA_OK:
+            raise RuntimeError(fa.fa_last_error())
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    flop = blocks * 4 * 4 * iters * 32768.0  # waves x chains x iters x flop per product
+    return flop / (best * 1e-3) / 1e12
 
 
 def cpu_baseline(w, q, k, v, do, max_workers: int = 16):
@@ -136,6 +156,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the products-only MFMA throughput probe (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -244,6 +266,18 @@ def main() -> int:
         kv_name = "bwd_dkdv8_kernel" if w.d <= 128 else "bwd_dkdv_kernel"
         kernels[kv_name] = (avg(kv_ms), 2.0 * F, "fa_bwd.hip")
         kernels["bwd_dq_kernel"] = (avg(q_ms), 1.5 * F, "fa_bwd.hip")
+    med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
+    stats = {"fwd": fwd_ms}
+    if bwd:
+        stats.update({"bwd": bwd_ms, "bwd_pre": pre_ms, "bwd_dkdv": kv_ms, "bwd_dq": q_ms})
+    out["kernel_ms"] = {n: {"mean": avg(xs), "median": med(xs), "min": min(xs)}
+                        for n, xs in stats.items()}
+    probe = None
+    if w.dtype == "bf16" and not args.no_mfma_probe:
+        probe = mfma_probe(fa, torch, dev, stream)
+        out["mfma_probe_tflops"] = probe
+        # the clock the probe implies: peak is 1024 flop / clock / SIMD x 1024 SIMDs
+        out["mfma_probe_implied_sclk_mhz"] = probe * 1e12 / (1024 * 1024) / 1e6
     if w.dtype == "bf16":
         name = max(kernels, key=lambda n: kernels[n][0])
         ms, flop, src = kernels[name]
@@ -257,7 +291,9 @@ def main() -> int:
             "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
             "traffic": _traffic(name, w.name, src),
             "avg_launch_ms": ms,
+            "frac_of_measured_mfma": achieved / probe if probe else None,
         }
+        out["fwd_frac_of_measured_mfma"] = out["fwd_tflops"] / probe if probe else None
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -123,6 +123,13 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   return launched("fa_bwd", fa::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 
+fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
+  if (!out) return fail(FA_ERR_INVALID_ARG, "fa_mfma_probe: null pointer");
+  if (blocks <= 0 || iters <= 0)
+    return fail(FA_ERR_INVALID_ARG, "fa_mfma_probe: blocks and iters must be positive");
+  return launched("fa_mfma_probe", fa::launch_mfma_probe(out, blocks, iters, (hipStream_t)stream));
+}
+
 fa_status fa_bwd_time_main_kernel(void* start_event, void* stop_event) {
   if ((start_event == nullptr) != (stop_event == nullptr))
     return fail(FA_ERR_INVALID_ARG, "fa_bwd_time_main_kernel: give both events or neither");

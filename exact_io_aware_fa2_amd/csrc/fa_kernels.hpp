@@ -42,5 +42,6 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
+hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
 
 }  // namespace fa

@@ -22,7 +22,7 @@ _lib = None
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 
 EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_bwd_workspace_size",
-            "fa_bwd_time_main_kernel", "fa_last_error", "fa_version")
+            "fa_bwd_time_main_kernel", "fa_mfma_probe", "fa_last_error", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -55,6 +55,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd.restype = i
     lib.fa_bwd_time_main_kernel.argtypes = [vp, vp]
     lib.fa_bwd_time_main_kernel.restype = i
+    lib.fa_mfma_probe.argtypes = [vp, i, i, vp]
+    lib.fa_mfma_probe.restype = i
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -114,6 +116,10 @@ def fa_bwd_time_main_kernel(start_event, stop_event) -> int:
             return e
         return e.cuda_event
     return load().fa_bwd_time_main_kernel(handle(start_event), handle(stop_event))
+
+
+def fa_mfma_probe(out, blocks, iters, stream=None) -> int:
+    return load().fa_mfma_probe(_ptr(out), int(blocks), int(iters), _stream(stream))
 
 
 def fa_last_error() -> str:

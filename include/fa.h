@@ -110,6 +110,16 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  */
 fa_status fa_bwd_time_main_kernel(void* start_event, void* stop_event);
 
+/*
+ * Measurement aid (no counterpart on the pages): enqueue `blocks` workgroups of 256
+ * threads, each wave running four independent chains of `iters` bf16 32x32x16 matrix-core
+ * products (32768 flop each; 4 waves per workgroup), so the sustained matrix throughput is
+ * blocks * 4 * 4 * iters * 32768 flop / elapsed time.  `out` is a caller-owned device buffer
+ * of blocks * 256 floats that receives per-lane sums (values are meaningless).  Returns
+ * FA_ERR_INVALID_ARG for a null `out` or non-positive sizes, FA_ERR_HIP on launch failure.
+ */
+fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream);
+
 /* Message for the last non-FA_OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);
 

@@ -99,3 +99,10 @@ def test_workspace_linear_in_n():
         assert s == ((2 * 8 * n * 4 + 255) // 256) * 256
     assert sizes[2] - sizes[1] == 2 * (sizes[1] - sizes[0])
     assert fa.fa_bwd_workspace_size(1, 1, 1, 3, 64, 0, 0) == 256
+
+
+def test_mfma_probe_validation():
+    # argument checks happen before any launch, so no GPU is touched
+    assert fa.fa_mfma_probe(None, 4, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_mfma_probe(1 << 20, 0, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_mfma_probe(1 << 20, 4, -1, stream=0) == fa.FA_ERR_INVALID_ARG
