@@ -416,31 +416,34 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     dv[i] = zero16();
   }
 
-  // Staging tasks of a step: [0, T1) = 4 rows x 8 dims of Q, [T1, 2 T1) = the same of dO;
-  // each stored row-major and transposed.
+  // Staging tasks of a step: 2 rows x 8 dims each, [0, T2) of Q and [T2, 2 T2) of dO, one
+  // per thread, so all eight waves share the staging; each is stored row-major and
+  // transposed.  Row pairs run fastest inside a wave: the row-major 16-byte stores of 8
+  // neighbouring lanes then hit distinct banks and the transposed 4-byte stores of 16
+  // neighbouring lanes fill one 64-byte run of a transposed row.
   constexpr int CPR = D / 8;
-  constexpr int T1 = (BQ / 4) * CPR;
-  static_assert(BQ % 16 == 0, "task_rc needs whole groups of 16 rows");
-  static_assert(2 * T1 <= NT, "one staging task per thread");
-  static_assert(T1 % 64 == 0, "Q and dO tasks fall on whole waves");
+  constexpr int T2 = (BQ / 2) * CPR;
+  static_assert(2 * T2 <= NT, "one staging task per thread");
+  static_assert(T2 % 64 == 0, "Q and dO tasks fall on whole waves");
   // Which operand a wave stages is wave-uniform, so its buffer resource stays scalar.
-  const bool stager = w < 2 * T1 / 64, iso = w >= T1 / 64;
+  const bool stager = w < 2 * T2 / 64, iso = w >= T2 / 64;
+  const int tt = iso ? tid - T2 : tid;
+  const int rp = tt % (BQ / 2), dc = tt / (BQ / 2);  // row pair, 8-dim chunk
   // Every thread fetches the LSE / D value of row tid % BQ of the step, unconditionally and
   // unscaled: a load consumed only at the next step's LDS write must not sit on a branch
   // merge or feed arithmetic right away, or the wait for it lands right behind its issue.
-  uint4 xr[4];
+  uint4 xr[2];
   float lraw = 0.f, draw = 0.f;
   auto step_r0 = [&](int it) { return (qb_lo + it % nq) * BQ; };
   auto gload = [&](int it) {
     const int g = it / nq, hq = hkv * G + g, r0 = step_r0(it);
     if (stager) {
-      const int t = iso ? tid - T1 : tid;
-      int rg, dc;
-      task_rc<CPR>(t, rg, dc);
       const bf16_t* base = (iso ? dO : Q) + ((size_t)b * N * Hq + hq) * D + (size_t)r0 * qs;
       const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
-      bload_4x8(xr, make_rsrc(base, bytes), (uint32_t)(4 * rg * qs + 8 * dc) * 2u,
-                (uint32_t)qs * 2u);
+      const rsrc_t res = make_rsrc(base, bytes);
+      const uint32_t off = (uint32_t)(2 * rp * qs + 8 * dc) * 2u;
+      xr[0] = bload16(res, off);
+      xr[1] = bload16(res, off + (uint32_t)qs * 2u);
     }
     const size_t l0 = ((size_t)b * Hq + hq) * N + r0;
     const uint32_t lbytes = (uint32_t)(N - r0) * 4u;
@@ -457,11 +460,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     bf16_t* sOT = sQT + Cfg::SQT;
     float* sL = reinterpret_cast<float*>(sOT + Cfg::SQT);
     if (stager) {
-      const int t = iso ? tid - T1 : tid;
-      int rg, dc;
-      task_rc<CPR>(t, rg, dc);
-      store_4x8_rows(iso ? sO : sQ, STR, 4 * rg, 8 * dc, xr);
-      store_4x8_transposed(iso ? sOT : sQT, TSTR, 4 * rg, 8 * dc, xr);
+      bf16_t* rdst = (iso ? sO : sQ) + (2 * rp) * STR + 8 * dc;
+      *reinterpret_cast<uint4*>(rdst) = xr[0];
+      *reinterpret_cast<uint4*>(rdst + STR) = xr[1];
+      // column 8 dc + j of the two rows -> one 32-bit word of transposed row 8 dc + j
+      bf16_t* tdst = (iso ? sOT : sQT) + (8 * dc) * TSTR + tpos(2 * rp);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t a0 = u4word(xr[0], m), a1 = u4word(xr[1], m);
+        *reinterpret_cast<uint32_t*>(tdst + (2 * m) * TSTR) = pack_lo(a0, a1);
+        *reinterpret_cast<uint32_t*>(tdst + (2 * m + 1) * TSTR) = pack_hi(a0, a1);
+      }
     }
     if (tid < BQ) {
       const bool in = step_r0(it) + tid < N;
