@@ -662,27 +662,46 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   const int klo = window > 0 ? row - window + 1 : 0;  // allowed keys of this row: [klo, khi]
   const int khi = causal ? min(row, N - 1) : N - 1;
 
-  // Staging tasks: [0, TK) = 4 keys x 8 dims of K (row-major + transposed),
-  // [TK, 2 TK) = the same of V (row-major).
+  // Staging.  d <= 128: every thread takes one 2-key x 8-dim task of K (stored row-major
+  // and transposed) and the same task of V (row-major), key pairs fastest inside a wave,
+  // so the work is even over the waves and the stores are free of bank conflicts.
+  // d = 256: 4-key x 8-dim tasks, [0, TK) of K and [TK, 2 TK) of V.
   constexpr int CPR = D / 8;
+  constexpr bool kPairs = D <= 128;
+  constexpr int TP = (BN / 2) * CPR;  // 2-key tasks per operand
+  static_assert(!kPairs || TP <= NT, "one 2-key task of K and of V per thread");
   constexpr int TK = (BN / 4) * CPR;
   static_assert(BN % 16 == 0, "task_rc needs whole groups of 16 rows");
-  constexpr int PT = (2 * TK + NT - 1) / NT;
-  static_assert(TK % 64 == 0, "K and V tasks fall on whole waves");
+  constexpr int PT = kPairs ? 1 : (2 * TK + NT - 1) / NT;
+  static_assert(kPairs || TK % 64 == 0, "K and V tasks fall on whole waves");
   uint4 xr[PT][4];
+  const int kp_ = tid % (BN / 2), dcp = tid / (BN / 2);  // key pair, 8-dim chunk
+  const bool ptask = TP == NT || tid < TP;
   auto gload = [&](int nb) {
+    const uint32_t bytes = (uint32_t)(N - nb * BN) * (uint32_t)ks * 2u;  // rows past N read 0
+    if constexpr (kPairs) {
+      if (ptask) {
+        const rsrc_t kres = make_rsrc(Kh + (size_t)nb * BN * ks, bytes);
+        const rsrc_t vres = make_rsrc(Vh + (size_t)nb * BN * ks, bytes);
+        const uint32_t off = (uint32_t)(2 * kp_ * ks + 8 * dcp) * 2u;
+        xr[0][0] = bload16(kres, off);
+        xr[0][1] = bload16(kres, off + (uint32_t)ks * 2u);
+        xr[0][2] = bload16(vres, off);
+        xr[0][3] = bload16(vres, off + (uint32_t)ks * 2u);
+      }
+    } else {
 #pragma unroll
-    for (int p = 0; p < PT; ++p) {
-      const int task = tid + NT * p;
-      const int wtask = 64 * w + NT * p;  // first task of this wave: wave-uniform
-      if ((2 * TK) % NT == 0 || wtask < 2 * TK) {
-        const bool isv = wtask >= TK;  // wave-uniform, keeps the buffer resource scalar
-        const int t = isv ? task - TK : task;
-        int kg, dc;
-        task_rc<CPR>(t, kg, dc);
-        const uint32_t bytes = (uint32_t)(N - nb * BN) * (uint32_t)ks * 2u;  // rows past N read 0
-        const rsrc_t res = make_rsrc((isv ? Vh : Kh) + (size_t)nb * BN * ks, bytes);
-        bload_4x8(xr[p], res, (uint32_t)(4 * kg * ks + 8 * dc) * 2u, (uint32_t)ks * 2u);
+      for (int p = 0; p < PT; ++p) {
+        const int task = tid + NT * p;
+        const int wtask = 64 * w + NT * p;  // first task of this wave: wave-uniform
+        if ((2 * TK) % NT == 0 || wtask < 2 * TK) {
+          const bool isv = wtask >= TK;  // wave-uniform, keeps the buffer resource scalar
+          const int t = isv ? task - TK : task;
+          int kg, dc;
+          task_rc<CPR>(t, kg, dc);
+          const rsrc_t res = make_rsrc((isv ? Vh : Kh) + (size_t)nb * BN * ks, bytes);
+          bload_4x8(xr[p], res, (uint32_t)(4 * kg * ks + 8 * dc) * 2u, (uint32_t)ks * 2u);
+        }
       }
     }
   };
@@ -690,19 +709,38 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
     bf16_t* sK = lds + buf * Cfg::BUF;
     bf16_t* sV = sK + Cfg::SK;
     bf16_t* sKT = sV + Cfg::SK;
+    if constexpr (kPairs) {
+      if (ptask) {
+        bf16_t* kdst = sK + (2 * kp_) * KSTR + 8 * dcp;
+        bf16_t* vdst = sV + (2 * kp_) * KSTR + 8 * dcp;
+        *reinterpret_cast<uint4*>(kdst) = xr[0][0];
+        *reinterpret_cast<uint4*>(kdst + KSTR) = xr[0][1];
+        *reinterpret_cast<uint4*>(vdst) = xr[0][2];
+        *reinterpret_cast<uint4*>(vdst + KSTR) = xr[0][3];
+        // column 8 dcp + j of the two keys -> one 32-bit word of K^T row 8 dcp + j
+        bf16_t* tdst = sKT + (8 * dcp) * TSTR + tpos(2 * kp_);
 #pragma unroll
-    for (int p = 0; p < PT; ++p) {
-      const int task = tid + NT * p;
-      if ((2 * TK) % NT == 0 || task < 2 * TK) {
-        const bool isv = task >= TK;
-        const int t = isv ? task - TK : task;
-        int kg, dc;
-        task_rc<CPR>(t, kg, dc);
-        if (isv) {
-          store_4x8_rows(sV, KSTR, 4 * kg, 8 * dc, xr[p]);
-        } else {
-          store_4x8_rows(sK, KSTR, 4 * kg, 8 * dc, xr[p]);
-          store_4x8_transposed(sKT, TSTR, 4 * kg, 8 * dc, xr[p]);
+        for (int m = 0; m < 4; ++m) {
+          const uint32_t a0 = u4word(xr[0][0], m), a1 = u4word(xr[0][1], m);
+          *reinterpret_cast<uint32_t*>(tdst + (2 * m) * TSTR) = pack_lo(a0, a1);
+          *reinterpret_cast<uint32_t*>(tdst + (2 * m + 1) * TSTR) = pack_hi(a0, a1);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PT; ++p) {
+        const int task = tid + NT * p;
+        if ((2 * TK) % NT == 0 || task < 2 * TK) {
+          const bool isv = task >= TK;
+          const int t = isv ? task - TK : task;
+          int kg, dc;
+          task_rc<CPR>(t, kg, dc);
+          if (isv) {
+            store_4x8_rows(sV, KSTR, 4 * kg, 8 * dc, xr[p]);
+          } else {
+            store_4x8_rows(sK, KSTR, 4 * kg, 8 * dc, xr[p]);
+            store_4x8_transposed(sKT, TSTR, 4 * kg, 8 * dc, xr[p]);
+          }
         }
       }
     }
