@@ -63,6 +63,25 @@ fa_status launched(const char* fn, hipError_t e) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Packed sequences: the shared checks on (Hq, Hkv, d, window, scale) run as for one batch
+// entry of `total` rows; on top, the offsets pointer, counts and grid size are checked.
+// The offsets themselves live on the device and are not read here (the kernels clamp
+// them into the tensors).
+fa_status check_varlen(const char* fn, const int* cu, int num_seqs, int total, int max_seqlen,
+                       int Hq, int Hkv, int d, int causal, int window, float scale) {
+  if (!cu) return fail(FA_ERR_INVALID_ARG, "%s: null cu_seqlens", fn);
+  if (num_seqs <= 0 || total <= 0 || max_seqlen <= 0)
+    return fail(FA_ERR_INVALID_ARG, "%s: num_seqs=%d, total=%d, max_seqlen=%d must be positive",
+                fn, num_seqs, total, max_seqlen);
+  if (max_seqlen > total)
+    return fail(FA_ERR_INVALID_ARG, "%s: max_seqlen=%d exceeds total=%d", fn, max_seqlen, total);
+  fa_status st = check_common(fn, 1, Hq, Hkv, total, d, causal, window, scale);
+  if (st != FA_OK) return st;
+  if ((int64_t)num_seqs * Hq * ((max_seqlen + 31) / 32) >= kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "%s: num_seqs * Hq * max_seqlen too large for one grid", fn);
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -128,6 +147,50 @@ fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
   if (blocks <= 0 || iters <= 0)
     return fail(FA_ERR_INVALID_ARG, "fa_mfma_probe: blocks and iters must be positive");
   return launched("fa_mfma_probe", fa::launch_mfma_probe(out, blocks, iters, (hipStream_t)stream));
+}
+
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
+                        int Hkv, int d, int causal, int window, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse)
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: null pointer");
+  fa_status st = check_varlen("fa_fwd_varlen", cu_seqlens, num_seqs, total, max_seqlen, Hq,
+                              Hkv, d, causal, window, scale);
+  if (st != FA_OK) return st;
+  const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;  // as in fa_fwd
+  fa::FwdArgs a{q, k, v, o, lse, num_seqs, Hq, Hkv, max_seqlen, d, causal ? 1 : 0, window,
+                c2, scale * fa::kHostLog2e, scale < 0.f ? 1 : 0, cu_seqlens, total};
+  return launched("fa_fwd_varlen", fa::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+size_t fa_bwd_varlen_workspace_size(int total, int Hq, int Hkv, int d) {
+  if (total <= 0 || check_common("fa_bwd_varlen_workspace_size", 1, Hq, Hkv, total, d, 0, 0,
+                                 1.f) != FA_OK)
+    return 0;
+  return align256((size_t)Hq * total * sizeof(float));
+}
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                        const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
+                        int Hkv, int d, int causal, int window, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: null pointer");
+  fa_status st = check_varlen("fa_bwd_varlen", cu_seqlens, num_seqs, total, max_seqlen, Hq,
+                              Hkv, d, causal, window, scale);
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_varlen_workspace_size(total, Hq, Hkv, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "fa_bwd_varlen: workspace of %zu bytes needed, %zu given",
+                need, workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(FA_ERR_WORKSPACE, "fa_bwd_varlen: workspace must be 256-byte aligned");
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, static_cast<float*>(workspace), num_seqs, Hq,
+                Hkv, max_seqlen, d, causal ? 1 : 0, window, scale, scale * fa::kHostLog2e,
+                g_time_start, g_time_stop, cu_seqlens, total};
+  g_time_start = g_time_stop = nullptr;
+  return launched("fa_bwd_varlen", fa::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 
 fa_status fa_bwd_time_main_kernel(void* start_event, void* stop_event) {

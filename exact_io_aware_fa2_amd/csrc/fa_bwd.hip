@@ -43,9 +43,10 @@ template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__ O,
                                                       const bf16_t* __restrict__ dO,
                                                       float* __restrict__ Dv, int B, int Hq,
-                                                      int N) {
+                                                      int N, const int* __restrict__ cu,
+                                                      int ntot) {
   constexpr int T = D / 8, RPB = 256 / T;
-  const long total = (long)B * N * Hq;
+  const long total = cu ? (long)ntot * Hq : (long)B * N * Hq;  // rows (token, head)
   const long r = (long)blockIdx.x * RPB + threadIdx.x / T;
   const int t = threadIdx.x % T;
   float sum = 0.f;
@@ -61,9 +62,13 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__
   for (int off = T / 2; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
   if (t == 0 && r < total) {
     const int hq = (int)(r % Hq);
-    const long bn = r / Hq;
-    const int n = (int)(bn % N), b = (int)(bn / N);
-    Dv[((long)b * Hq + hq) * N + n] = sum;
+    const long bn = r / Hq;  // token row
+    if (cu) {
+      Dv[(long)hq * ntot + bn] = sum;  // packed sequences: [Hq, total]
+    } else {
+      const int n = (int)(bn % N), b = (int)(bn / N);
+      Dv[((long)b * Hq + hq) * N + n] = sum;
+    }
   }
 }
 
@@ -89,8 +94,8 @@ template <int D>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
-    int causal, int window, float c, float scale) {
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int B, int Hq, int Hkv, int Nmax,
+    int causal, int window, float c, float scale, const int* __restrict__ cu, int ntot) {
   using Cfg = KVCfg<D>;
   constexpr int BKN = Cfg::BKN, BQ = Cfg::BQ, MT = Cfg::MT, DH = Cfg::DH;
   constexpr int NSPLIT = Cfg::NSPLIT, STR = Cfg::STR, TSTR = Cfg::TSTR;
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int BUFB = Cfg::BUF * 2 + 2 * BQ * 4;  // bytes per buffer
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int num_kb = (N + BKN - 1) / BKN;
+  const int num_kb = (Nmax + BKN - 1) / BKN;
   const int total = B * Hkv * num_kb * NSPLIT;
   const int lin = xcd_remap(blockIdx.x, total);
   const int split = lin % NSPLIT;
@@ -109,6 +114,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // longest first: causal -> low key blocks see the most rows; a pure left window -> high.
   const int kb = (!causal && window > 0) ? num_kb - 1 - kbo : kbo;
   const int b = head / Hkv, hkv = head - b * Hkv;
+  int seq0, N;  // first row and length of this batch entry's sequence
+  seq_span(cu, ntot, b, Nmax, seq0, N);
+  if (kb * BKN >= N) return;  // a key block past the end of a shorter packed sequence
   const int G = Hq / Hkv;
   const int dh0 = split * DH;
 
@@ -117,8 +125,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int n0 = kb * BKN, kw0 = n0 + 32 * w, key = kw0 + l32;
 
   const size_t qs = (size_t)Hq * D, ks = (size_t)Hkv * D;
-  const bf16_t* Kb = K + ((size_t)b * N * Hkv + hkv) * D;
-  const bf16_t* Vb = V + ((size_t)b * N * Hkv + hkv) * D;
+  const bf16_t* Kb = K + ((size_t)seq0 * Hkv + hkv) * D;
+  const bf16_t* Vb = V + ((size_t)seq0 * Hkv + hkv) * D;
 
   // B operands K^T and V^T of this lane's key.
   bf16x8 kop[NC], vop[NC];
@@ -154,8 +162,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   auto gload = [&](int it) {
     const int g = it / nq, qb = qb_lo + (it - g * nq);
     const int hq = hkv * G + g, r0 = qb * BQ;
-    const bf16_t* Qb = Q + ((size_t)b * N * Hq + hq) * D;
-    const bf16_t* Ob = dO + ((size_t)b * N * Hq + hq) * D;
+    const bf16_t* Qb = Q + ((size_t)seq0 * Hq + hq) * D;
+    const bf16_t* Ob = dO + ((size_t)seq0 * Hq + hq) * D;
     const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
     const rsrc_t qres = make_rsrc(Qb + (size_t)r0 * qs, bytes);
     const rsrc_t ores = make_rsrc(Ob + (size_t)r0 * qs, bytes);
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     }
     if (tid < BQ) {
       const int n = r0 + tid;
-      const size_t li = ((size_t)b * Hq + hq) * N + n;
+      const size_t li = stat_base(cu, ntot, b, Hq, hq, Nmax, seq0) + n;
       lreg = n < N ? LSE[li] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
       dreg = n < N ? Dv[li] : 0.f;
     }
@@ -320,8 +328,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   }
 
   if (key < N) {
-    bf16_t* dkr = dK + ((size_t)b * N + key) * ks + (size_t)hkv * D + dh0;
-    bf16_t* dvr = dV + ((size_t)b * N + key) * ks + (size_t)hkv * D + dh0;
+    bf16_t* dkr = dK + ((size_t)seq0 + key) * ks + (size_t)hkv * D + dh0;
+    bf16_t* dvr = dV + ((size_t)seq0 + key) * ks + (size_t)hkv * D + dh0;
 #pragma unroll
     for (int dt = 0; dt < NDH; ++dt) {
 #pragma unroll
@@ -364,8 +372,8 @@ template <int D>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int B, int Hq, int Hkv, int N,
-    int causal, int window, float c, float scale) {
+    bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int B, int Hq, int Hkv, int Nmax,
+    int causal, int window, float c, float scale, const int* __restrict__ cu, int ntot) {
   using Cfg = KV8Cfg<D>;
   constexpr int NT = Cfg::NT, BKN = Cfg::BKN, BQ = Cfg::BQ, STR = Cfg::STR, TSTR = Cfg::TSTR;
   constexpr int NC = D / 16, ND = D / 32;
@@ -373,13 +381,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   bf16_t* sV = reinterpret_cast<bf16_t*>(smem);
   char* stage = smem + Cfg::SV * 2;
 
-  const int num_kb = (N + BKN - 1) / BKN;
+  const int num_kb = (Nmax + BKN - 1) / BKN;
   const int total = B * Hkv * num_kb;
   const int lin = xcd_remap(blockIdx.x, total);
   const int head = lin / num_kb;
   const int kbo = lin - head * num_kb;
   const int kb = (!causal && window > 0) ? num_kb - 1 - kbo : kbo;  // longest first
   const int b = head / Hkv, hkv = head - b * Hkv;
+  int seq0, N;  // first row and length of this batch entry's sequence
+  seq_span(cu, ntot, b, Nmax, seq0, N);
+  if (kb * BKN >= N) return;  // a key block past the end of a shorter packed sequence
   const int G = Hq / Hkv;
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -387,8 +398,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   const int n0 = kb * BKN, kw0 = n0 + 32 * w, key = kw0 + l32;
 
   const size_t qs = (size_t)Hq * D, ks = (size_t)Hkv * D;
-  const bf16_t* Kb = K + ((size_t)b * N * Hkv + hkv) * D;
-  const bf16_t* Vb = V + ((size_t)b * N * Hkv + hkv) * D;
+  const bf16_t* Kb = K + ((size_t)seq0 * Hkv + hkv) * D;
+  const bf16_t* Vb = V + ((size_t)seq0 * Hkv + hkv) * D;
 
   // K^T B operand of this lane's key; the whole V block into LDS (row-major).
   bf16x8 kop[NC];
@@ -438,14 +449,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   auto gload = [&](int it) {
     const int g = it / nq, hq = hkv * G + g, r0 = step_r0(it);
     if (stager) {
-      const bf16_t* base = (iso ? dO : Q) + ((size_t)b * N * Hq + hq) * D + (size_t)r0 * qs;
+      const bf16_t* base = (iso ? dO : Q) + ((size_t)seq0 * Hq + hq) * D + (size_t)r0 * qs;
       const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
       const rsrc_t res = make_rsrc(base, bytes);
       const uint32_t off = (uint32_t)(2 * rp * qs + 8 * dc) * 2u;
       xr[0] = bload16(res, off);
       xr[1] = bload16(res, off + (uint32_t)qs * 2u);
     }
-    const size_t l0 = ((size_t)b * Hq + hq) * N + r0;
+    const size_t l0 = stat_base(cu, ntot, b, Hq, hq, Nmax, seq0) + r0;
     const uint32_t lbytes = (uint32_t)(N - r0) * 4u;
     const uint32_t loff = (uint32_t)(tid % BQ) * 4u;
     lraw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -576,8 +587,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   }
 
   if (key < N) {
-    bf16_t* dkr = dK + ((size_t)b * N + key) * ks + (size_t)hkv * D;
-    bf16_t* dvr = dV + ((size_t)b * N + key) * ks + (size_t)hkv * D;
+    bf16_t* dkr = dK + ((size_t)seq0 + key) * ks + (size_t)hkv * D;
+    bf16_t* dvr = dV + ((size_t)seq0 + key) * ks + (size_t)hkv * D;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
 #pragma unroll
@@ -615,21 +626,24 @@ template <int D>
 __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16_t* __restrict__ dQ, int B, int Hq, int Hkv, int N, int causal, int window, float c,
-    float scale) {
+    bf16_t* __restrict__ dQ, int B, int Hq, int Hkv, int Nmax, int causal, int window, float c,
+    float scale, const int* __restrict__ cu, int ntot) {
   using Cfg = QCfg<D>;
   constexpr int NT = Cfg::NT, BM = Cfg::BM, BN = Cfg::BN, KSTR = Cfg::KSTR, TSTR = Cfg::TSTR;
   constexpr int NC = D / 16, ND = D / 32;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
 
-  const int num_m = (N + BM - 1) / BM;
+  const int num_m = (Nmax + BM - 1) / BM;
   const int total = B * Hq * num_m;
   const int lin = xcd_remap(blockIdx.x, total);
   const int head = lin / num_m;
   const int mb = num_m - 1 - (lin - head * num_m);
   const int b = head / Hq, hq = head - b * Hq;
   const int hkv = hq / (Hq / Hkv);
+  int seq0, N;  // first row and length of this batch entry's sequence
+  seq_span(cu, ntot, b, Nmax, seq0, N);
+  if (mb * BM >= N) return;  // a row block past the end of a shorter packed sequence
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int hh = lane >> 5, l32 = lane & 31;
@@ -638,10 +652,10 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   const int row = wr0 + l32;
 
   const size_t qs = (size_t)Hq * D, ks = (size_t)Hkv * D;
-  const bf16_t* Qh = Q + ((size_t)b * N * Hq + hq) * D;
-  const bf16_t* Oh = dO + ((size_t)b * N * Hq + hq) * D;
-  const bf16_t* Kh = K + ((size_t)b * N * Hkv + hkv) * D;
-  const bf16_t* Vh = V + ((size_t)b * N * Hkv + hkv) * D;
+  const bf16_t* Qh = Q + ((size_t)seq0 * Hq + hq) * D;
+  const bf16_t* Oh = dO + ((size_t)seq0 * Hq + hq) * D;
+  const bf16_t* Kh = K + ((size_t)seq0 * Hkv + hkv) * D;
+  const bf16_t* Vh = V + ((size_t)seq0 * Hkv + hkv) * D;
 
   // B operands: this lane's rows of Q and dO.
   bf16x8 qop[NC], oop[NC];
@@ -651,7 +665,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
     qop[cc] = __builtin_bit_cast(bf16x8, row < N ? gload16(Qh + (size_t)row * qs + 16 * cc + 8 * hh) : z);
     oop[cc] = __builtin_bit_cast(bf16x8, row < N ? gload16(Oh + (size_t)row * qs + 16 * cc + 8 * hh) : z);
   }
-  const size_t li = ((size_t)b * Hq + hq) * N + row;
+  const size_t li = stat_base(cu, ntot, b, Hq, hq, Nmax, seq0) + row;
   const float lse2 = row < N ? LSE[li] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
   const float dval = row < N ? Dv[li] : 0.f;
 
@@ -848,7 +862,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   }
 
   if (row < N) {
-    bf16_t* qrow = dQ + ((size_t)b * N + row) * qs + (size_t)hq * D;
+    bf16_t* qrow = dQ + ((size_t)seq0 + row) * qs + (size_t)hq * D;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
 #pragma unroll
@@ -883,10 +897,11 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
     attr_done = true;
   }
-  const long rows = (long)a.B * a.N * a.Hq;
+  const long rows = a.cu ? (long)a.ntot * a.Hq : (long)a.B * a.N * a.Hq;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     st, (const bf16_t*)a.o, (const bf16_t*)a.dO, a.dvec, a.B, a.Hq, a.N);
+                     st, (const bf16_t*)a.o, (const bf16_t*)a.dO, a.dvec, a.B, a.Hq, a.N, a.cu,
+                     a.ntot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_start) {
@@ -900,14 +915,14 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
                        K8::LDS_BYTES, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
                        (const bf16_t*)a.v, (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dk,
                        (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window,
-                       a.c_log2_signed, a.scale);
+                       a.c_log2_signed, a.scale, a.cu, a.ntot);
   } else {
     const int num_kb = (a.N + KC::BKN - 1) / KC::BKN;
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * num_kb * KC::NSPLIT),
                        dim3(KC::NT), KC::LDS_BYTES, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
                        (const bf16_t*)a.v, (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dk,
                        (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window,
-                       a.c_log2_signed, a.scale);
+                       a.c_log2_signed, a.scale, a.cu, a.ntot);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -919,7 +934,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.B * a.Hq * num_m), dim3(QC::NT), QC::LDS_BYTES, st,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
                      (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N,
-                     a.causal, a.window, a.c_log2_signed, a.scale);
+                     a.causal, a.window, a.c_log2_signed, a.scale, a.cu, a.ntot);
   return hipGetLastError();
 }
 

@@ -126,6 +126,30 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Row span of batch entry b.  Fixed-length batches (cu == nullptr) occupy rows
+// b * nmax .. b * nmax + nmax - 1 of the tensors; packed sequences occupy rows
+// cu[b] .. cu[b + 1] - 1, clamped to [0, ntot) and to at most nmax rows, so a malformed
+// offset array can shorten a sequence but never move an access out of the tensors.
+__device__ __forceinline__ void seq_span(const int* cu, int ntot, int b, int nmax, int& start,
+                                         int& len) {
+  if (cu == nullptr) {
+    start = b * nmax;
+    len = nmax;
+    return;
+  }
+  const int s0 = min(max(cu[b], 0), ntot);
+  const int s1 = min(max(cu[b + 1], s0), ntot);
+  start = s0;
+  len = min(s1 - s0, nmax);
+}
+
+// Offset of row 0 of (batch entry b, query head hq) in the float32 row statistics (LSE,
+// D): [B, Hq, nmax] for fixed-length batches, [Hq, ntot] for packed sequences.
+__device__ __forceinline__ size_t stat_base(const int* cu, int ntot, int b, int Hq, int hq,
+                                            int nmax, int start) {
+  return cu == nullptr ? ((size_t)b * Hq + hq) * nmax : (size_t)hq * ntot + start;
+}
+
 // Index of the calling wave inside its workgroup, as a scalar (wave-uniform) value.
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

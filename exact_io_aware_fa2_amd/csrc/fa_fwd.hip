@@ -63,8 +63,8 @@ __device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1)
 template <int D>
 __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
-    bf16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int N,
-    int causal, int window, float c, int neg_q) {
+    bf16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Nmax,
+    int causal, int window, float c, int neg_q, const int* __restrict__ cu, int ntot) {
   using Cfg = FwdCfg<D>;
   constexpr int NT = Cfg::NT, BM = Cfg::BM, BN = Cfg::BN, KSTR = Cfg::KSTR, VSTR = Cfg::VSTR;
   constexpr int NC = D / 16;  // k-steps of S^T over the head dim
@@ -72,13 +72,17 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
 
-  const int num_m = (N + BM - 1) / BM;
+  const int num_m = (Nmax + BM - 1) / BM;
   const int total = B * Hq * num_m;
   const int lin = xcd_remap(blockIdx.x, total);
   const int head = lin / num_m;
   const int mb = num_m - 1 - (lin - head * num_m);
   const int b = head / Hq, hq = head - b * Hq;
   const int hkv = hq / (Hq / Hkv);
+  int seq0, N;  // first row and length of this batch entry's sequence
+  seq_span(cu, ntot, b, Nmax, seq0, N);
+  if (mb * BM >= N) return;  // a row block past the end of a shorter packed sequence
+  const size_t lse0 = stat_base(cu, ntot, b, Hq, hq, Nmax, seq0);
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int hh = lane >> 5, l32 = lane & 31;
@@ -87,9 +91,9 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   const int row = wr0 + l32;
 
   const size_t qs = (size_t)Hq * D, ks = (size_t)Hkv * D;
-  const bf16_t* Qh = Q + ((size_t)b * N * Hq + hq) * D;
-  const bf16_t* Kh = K + ((size_t)b * N * Hkv + hkv) * D;
-  const bf16_t* Vh = V + ((size_t)b * N * Hkv + hkv) * D;
+  const bf16_t* Qh = Q + ((size_t)seq0 * Hq + hq) * D;
+  const bf16_t* Kh = K + ((size_t)seq0 * Hkv + hkv) * D;
+  const bf16_t* Vh = V + ((size_t)seq0 * Hkv + hkv) * D;
 
   // Q^T operand: lane holds Q[row][16c + 8hh .. +7] for every k-step c.
   bf16x8 qop[NC];
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   const float le = half_sum(le_i);
   if (row < N) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    bf16_t* orow = O + ((size_t)b * N + row) * qs + (size_t)hq * D;
+    bf16_t* orow = O + ((size_t)seq0 + row) * qs + (size_t)hq * D;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
 #pragma unroll
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
       }
     }
     if (hh == 0)
-      LSE[((size_t)b * Hq + hq) * N + row] = le > 0.f ? (m_i + __log2f(le)) * kLn2 : -INFINITY;
+      LSE[lse0 + row] = le > 0.f ? (m_i + __log2f(le)) * kLn2 : -INFINITY;
   }
 }
 
@@ -455,7 +459,8 @@ static hipError_t launch_fwd_bf16_d(const FwdArgs& a, hipStream_t st) {
   const int grid = a.B * a.Hq * num_m;
   hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(grid), dim3(Cfg::NT), Cfg::LDS_BYTES, st,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (bf16_t*)a.o,
-                     a.lse, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window, a.c_log2, a.neg_q);
+                     a.lse, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window, a.c_log2, a.neg_q, a.cu,
+                     a.ntot);
   return hipGetLastError();
 }
 

@@ -15,10 +15,12 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int B, Hq, Hkv, N, d, causal, window;
+  int B, Hq, Hkv, N, d, causal, window;  // packed sequences: B sequences, N = max length
   float c_log2;         // |scale| * log2(e)
   float c_log2_signed;  // scale * log2(e)
   int neg_q;            // 1 when scale < 0 (Q is negated exactly inside the kernel)
+  const int* cu;        // packed sequences: B + 1 row offsets (device); null: fixed length
+  int ntot;             // packed sequences: rows of the packed tensors
 };
 
 struct BwdArgs {
@@ -31,12 +33,14 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;  // D = rowsum(dO * O), [B, Hq, N]
-  int B, Hq, Hkv, N, d, causal, window;
+  float* dvec;  // D = rowsum(dO * O), laid out like LSE
+  int B, Hq, Hkv, N, d, causal, window;  // packed sequences: B sequences, N = max length
   float scale;
   float c_log2_signed;  // scale * log2(e)
   hipEvent_t ev_start;  // optional events recorded around the key-block kernel (may be null)
   hipEvent_t ev_stop;
+  const int* cu;        // packed sequences: B + 1 row offsets (device); null: fixed length
+  int ntot;             // packed sequences: rows of the packed tensors
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);

@@ -21,8 +21,9 @@ _lib = None
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_bwd_workspace_size",
-            "fa_bwd_time_main_kernel", "fa_mfma_probe", "fa_last_error", "fa_version")
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_varlen",
+            "fa_bwd_varlen", "fa_bwd_varlen_workspace_size", "fa_bwd_time_main_kernel",
+            "fa_mfma_probe", "fa_last_error", "fa_version")
 
 
 class FaError(RuntimeError):
@@ -53,6 +54,13 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_bwd.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_varlen.restype = i
+    lib.fa_bwd_varlen_workspace_size.argtypes = [i, i, i, i]
+    lib.fa_bwd_varlen_workspace_size.restype = sz
+    lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
+                                  i, f, vp, sz, vp]
+    lib.fa_bwd_varlen.restype = i
     lib.fa_bwd_time_main_kernel.argtypes = [vp, vp]
     lib.fa_bwd_time_main_kernel.restype = i
     lib.fa_mfma_probe.argtypes = [vp, i, i, vp]
@@ -106,6 +114,25 @@ def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, sc
     return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq),
                          _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal), int(window),
                          float(scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, total, max_seqlen, Hq, Hkv, d, causal,
+                  window, scale, stream=None) -> int:
+    return load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
+                                num_seqs, total, max_seqlen, Hq, Hkv, d, int(causal),
+                                int(window), float(scale), _stream(stream))
+
+
+def fa_bwd_varlen_workspace_size(total, Hq, Hkv, d) -> int:
+    return load().fa_bwd_varlen_workspace_size(total, Hq, Hkv, d)
+
+
+def fa_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, num_seqs, total, max_seqlen, Hq,
+                  Hkv, d, causal, window, scale, workspace, workspace_bytes, stream=None) -> int:
+    return load().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                                _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), num_seqs, total,
+                                max_seqlen, Hq, Hkv, d, int(causal), int(window), float(scale),
+                                _ptr(workspace), int(workspace_bytes), _stream(stream))
 
 
 def fa_bwd_time_main_kernel(start_event, stop_event) -> int:
@@ -185,3 +212,53 @@ def backward(q, k, v, o, dO, lse, causal=False, window=0, scale=None, dq=None, d
 def dvec_from_workspace(workspace: torch.Tensor, B: int, Hq: int, N: int) -> torch.Tensor:
     """View of D = rowsum(dO * O) ([B, Hq, N] float32) at the start of the workspace."""
     return workspace[: B * Hq * N * 4].view(torch.float32).view(B, Hq, N)
+
+
+# ------------------------------------------------------------ packed sequences
+def _shapes_varlen(q, k, v, cu_seqlens):
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("packed q, k, v must be [total, heads, headdim]")
+    T, Hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != T or k.shape[2] != d:
+        raise ValueError(f"shape mismatch q={tuple(q.shape)} k={tuple(k.shape)} v={tuple(v.shape)}")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
+        raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
+    for t in (q, k, v, cu_seqlens):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return T, Hq, k.shape[1], d, cu_seqlens.numel() - 1
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, scale=None,
+                   out=None, lse=None, stream=None):
+    """O [total, Hq, d], LSE [Hq, total] for packed bf16 sequences."""
+    T, Hq, Hkv, d, S = _shapes_varlen(q, k, v, cu_seqlens)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Hq, T), device=q.device, dtype=torch.float32) if lse is None else lse
+    _check(fa_fwd_varlen(q, k, v, out, lse, cu_seqlens, S, T, max_seqlen, Hq, Hkv, d, causal,
+                         window, scale, stream))
+    return out, lse
+
+
+def workspace_for_varlen(total, Hq, Hkv, d, device) -> torch.Tensor:
+    nbytes = fa_bwd_varlen_workspace_size(total, Hq, Hkv, d)
+    if nbytes == 0:
+        raise FaError(FA_ERR_INVALID_ARG, fa_last_error())
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def backward_varlen(q, k, v, o, dO, lse, cu_seqlens, max_seqlen, causal=False, window=0,
+                    scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """dQ, dK, dV of L = sum(O * dO) for packed bf16 sequences."""
+    T, Hq, Hkv, d, S = _shapes_varlen(q, k, v, cu_seqlens)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = workspace_for_varlen(T, Hq, Hkv, d, q.device)
+    _check(fa_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, S, T, max_seqlen, Hq, Hkv,
+                         d, causal, window, scale, workspace,
+                         workspace.numel() * workspace.element_size(), stream))
+    return dq, dk, dv

@@ -105,3 +105,79 @@ def small_case(name: str, dtype: str, B: int, Hq: int, Hkv: int, N: int, d: int,
     """A parity-test workload of arbitrary (small) shape."""
     return Workload(name, dtype, B, Hq, Hkv, N, d, causal, window, sigma_qk, sigma_qk,
                     seed=seed)
+
+
+# ------------------------------------------------------------------ packed sequences
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """Sequences of different lengths packed back to back (no padding), bf16.
+
+    Tensors are [total, heads, headdim]; sequence s owns rows cu[s] .. cu[s+1]-1.
+    """
+    name: str
+    lengths: tuple
+    Hq: int
+    Hkv: int
+    d: int
+    causal: bool
+    window: int = 0
+    seed: int = 2000
+
+    @property
+    def total(self) -> int:
+        return int(sum(self.lengths))
+
+    @property
+    def max_seqlen(self) -> int:
+        return max(1, int(max(self.lengths)))
+
+    @property
+    def cu_seqlens(self) -> list:
+        out = [0]
+        for n in self.lengths:
+            out.append(out[-1] + int(n))
+        return out
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+
+def length_mix(total: int, lo: int, hi: int, seed: int) -> tuple:
+    """Sequence lengths drawn log-uniformly in [lo, hi] until they fill ``total`` rows
+    (the last one is cut to fit): a mix of short and long documents."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    out, left = [], total
+    while left > 0:
+        u = torch.rand((), generator=g, dtype=torch.float64).item()
+        n = int(round(math.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))))
+        n = max(1, min(n, left))
+        out.append(n)
+        left -= n
+    return tuple(out)
+
+
+# A packed batch with the headline's token count (2 x 8192 rows of 32 heads, d=128,
+# causal), made of documents of 128 .. 8192 rows.
+VARLEN_WORKLOADS = {
+    "bf16_varlen_t16384_h32_d128_causal": VarlenWorkload(
+        "bf16_varlen_t16384_h32_d128_causal", length_mix(16384, 128, 8192, 2001), 32, 32, 128,
+        True, seed=2001),
+}
+
+
+def make_varlen_inputs(w: VarlenWorkload, device: str | torch.device = "cpu"):
+    """Draw packed (q, k, v, dO) in the order and manner of ``make_inputs``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+
+    def draw(h):
+        return torch.randn((w.total, h, w.d), generator=g, dtype=torch.float32).to(
+            torch.bfloat16).to(device)
+
+    q = draw(w.Hq)
+    k = draw(w.Hkv)
+    v = draw(w.Hkv)
+    do = draw(w.Hq)
+    return q, k, v, do

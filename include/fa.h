@@ -102,7 +102,41 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  size_t workspace_bytes, void* stream);
 
 /*
- * Benchmark hook (no counterpart on the pages): the next fa_bwd call made on this thread
+ * Packed variable-length sequences.  bmjup.com, "FlashAttention-2 ... 实战解析", FAQ Q4,
+ * names a variable-length interface beside the fixed-length one; what it computes is the
+ * attention above applied to each sequence on its own (self-attention inside a sequence,
+ * masks counted from the sequence's first row).
+ *   q, o, dO, dq [total, Hq, d] and k, v, dk, dv [total, Hkv, d], bfloat16, contiguous:
+ *                    sequence s occupies rows cu_seqlens[s] .. cu_seqlens[s + 1] - 1 of
+ *                    every tensor (the same rows for queries and keys)
+ *   cu_seqlens       device array of num_seqs + 1 int32 offsets, non-decreasing, first 0,
+ *                    last total (an empty sequence is allowed); caller-owned, read by the
+ *                    kernels only
+ *   max_seqlen       an upper bound on every sequence length, <= total.  The offsets are not
+ *                    read on the host: a sequence longer than max_seqlen is computed on its
+ *                    first max_seqlen rows only, and offsets outside [0, total] are clamped
+ *                    into it, so bad offsets give wrong values but no out-of-bounds access.
+ *   lse (and the workspace's D) float32 [Hq, total]
+ * Other arguments, the error codes and the stream rules are those of fa_fwd / fa_bwd
+ * (B = num_seqs and N = max_seqlen for the size checks); FA_ERR_INVALID_ARG also for a
+ * null cu_seqlens, non-positive counts or max_seqlen > total.
+ */
+fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
+                        int Hkv, int d, int causal, int window, float scale, void* stream);
+
+/* Workspace bytes for fa_bwd_varlen: D as float32 [Hq, total] rounded up to 256; 0 for
+ * invalid sizes. */
+size_t fa_bwd_varlen_workspace_size(int total, int Hq, int Hkv, int d);
+
+fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                        const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                        const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
+                        int Hkv, int d, int causal, int window, float scale, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Benchmark hook (no counterpart on the pages): the next fa_bwd (or fa_bwd_varlen) call made on this thread
  * records `start_event` on its stream right before its key-block kernel (dK, dV) and
  * `stop_event` right after it (the query-block kernel for dQ follows), so a caller can time
  * the backward kernels separately with hipEventElapsedTime.  Arguments are hipEvent_t handles owned by the caller; passing NULL

@@ -36,4 +36,6 @@ from .attention import (  # noqa: F401
     attn_bwd_dq_rows,
     attn_bwd_dkdv_cols,
     attended_pairs,
+    attn_fwd_varlen,
+    attn_bwd_varlen,
 )

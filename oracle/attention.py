@@ -345,3 +345,67 @@ def attended_pairs(n: int, causal: bool, window: int) -> int:
         lo, hi = allowed_keys(i, n, causal, window)
         total += max(0, hi - lo)
     return total
+
+
+# ------------------------------------------------------------------ packed sequences
+def _check_cu(cu_seqlens, total: int) -> np.ndarray:
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or cu[-1] != total or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must be non-decreasing offsets from 0 to total")
+    return cu
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, causal=False, window=0, scale=None,
+                    row_chunk=DEFAULT_ROW_CHUNK):
+    """Forward over packed sequences: q [T, Hq, d], k, v [T, Hkv, d].
+
+    Sequence s is rows cu_seqlens[s] .. cu_seqlens[s+1]-1 of every tensor.  It is the
+    plain attention above applied to each sequence by itself: its queries see only its own
+    keys, and the causal / window masks count positions from the sequence's first row.
+    (bmjup.com, FAQ Q4, names the variable-length interface; the packing is the reading
+    this code takes of it.)  Returns O [T, Hq, dv] and LSE [Hq, T], float64.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    t, hq, d = q.shape
+    hkv = k.shape[1]
+    cu = _check_cu(cu_seqlens, t)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    g = hq // hkv
+    o = np.zeros((t, hq, v.shape[2]))
+    lse = np.zeros((hq, t))
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        if s1 == s0:
+            continue
+        for h in range(hq):
+            oh, lh = attn_fwd_head(q[s0:s1, h], k[s0:s1, h // g], v[s0:s1, h // g], causal,
+                                   window, scale, row_chunk)
+            o[s0:s1, h] = oh
+            lse[h, s0:s1] = lh
+    return o, lse
+
+
+def attn_bwd_varlen(q, k, v, do, cu_seqlens, causal=False, window=0, scale=None,
+                    row_chunk=DEFAULT_ROW_CHUNK):
+    """Backward over packed sequences: (dQ [T,Hq,d], dK, dV [T,Hkv,d], D [Hq,T]), each
+    sequence on its own as in attn_fwd_varlen; dK, dV of a KV head summed over its group."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    t, hq, d = q.shape
+    hkv = k.shape[1]
+    cu = _check_cu(cu_seqlens, t)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    g = hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dvec = np.zeros((hq, t))
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        if s1 == s0:
+            continue
+        for h in range(hq):
+            dqh, dkh, dvh, dh = attn_bwd_head(q[s0:s1, h], k[s0:s1, h // g], v[s0:s1, h // g],
+                                              do[s0:s1, h], causal, window, scale, row_chunk)
+            dq[s0:s1, h] = dqh
+            dk[s0:s1, h // g] += dkh
+            dv[s0:s1, h // g] += dvh
+            dvec[h, s0:s1] = dh
+    return dq, dk, dv, dvec

@@ -106,3 +106,55 @@ def test_mfma_probe_validation():
     assert fa.fa_mfma_probe(None, 4, 4, stream=0) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_mfma_probe(1 << 20, 0, 4, stream=0) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_mfma_probe(1 << 20, 4, -1, stream=0) == fa.FA_ERR_INVALID_ARG
+
+
+BAD_VARLEN = [
+    (dict(cu=None), fa.FA_ERR_INVALID_ARG),
+    (dict(num_seqs=0), fa.FA_ERR_INVALID_ARG),
+    (dict(total=0), fa.FA_ERR_INVALID_ARG),
+    (dict(max_seqlen=0), fa.FA_ERR_INVALID_ARG),
+    (dict(max_seqlen=65), fa.FA_ERR_INVALID_ARG),  # longer than the packed rows
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(window=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(d=32), fa.FA_ERR_UNSUPPORTED),
+    (dict(num_seqs=1 << 20, total=1 << 20, max_seqlen=1 << 20, Hq=64, Hkv=64),
+     fa.FA_ERR_INVALID_ARG),
+]
+
+
+@pytest.mark.parametrize("bad,status", BAD_VARLEN)
+@pytest.mark.parametrize("entry", ["fa_fwd_varlen", "fa_bwd_varlen"])
+def test_varlen_validation(entry, bad, status):
+    a = dict(cu=256, num_seqs=3, total=64, max_seqlen=40, Hq=4, Hkv=2, d=128, causal=1,
+             window=0, scale=0.1)
+    a.update(bad)
+    fake = 256
+    common = (a["cu"], a["num_seqs"], a["total"], a["max_seqlen"], a["Hq"], a["Hkv"], a["d"],
+              a["causal"], a["window"], a["scale"])
+    if entry == "fa_fwd_varlen":
+        st = fa.fa_fwd_varlen(fake, fake, fake, fake, fake, *common, stream=0)
+    else:
+        st = fa.fa_bwd_varlen(fake, fake, fake, fake, fake, fake, fake, fake, fake, *common,
+                              4096, 1 << 30, stream=0)
+    assert st == status
+    assert fa.fa_last_error().startswith(entry)
+
+
+def test_varlen_workspace():
+    # D only: Hq * total float32, rounded up to 256 bytes
+    assert fa.fa_bwd_varlen_workspace_size(1000, 8, 2, 128) == ((8 * 1000 * 4 + 255) // 256) * 256
+    assert fa.fa_bwd_varlen_workspace_size(0, 8, 2, 128) == 0
+    assert fa.fa_bwd_varlen_workspace_size(64, 6, 4, 128) == 0
+    assert fa.fa_bwd_varlen_workspace_size(64, 4, 4, 96) == 0
+    fake = 256
+    need = fa.fa_bwd_varlen_workspace_size(64, 4, 2, 128)
+    args = (fake, 3, 64, 40, 4, 2, 128, 1, 0, 0.1)
+    st = fa.fa_bwd_varlen(*([fake] * 9), *args, 4096, need - 1, stream=0)
+    assert st == fa.FA_ERR_WORKSPACE
+    st = fa.fa_bwd_varlen(*([fake] * 9), *args, 4096 + 64, need, stream=0)
+    assert st == fa.FA_ERR_WORKSPACE
+    st = fa.fa_bwd_varlen(*([fake] * 9), *args, None, need, stream=0)
+    assert st == fa.FA_ERR_WORKSPACE
+    st = fa.fa_fwd_varlen(None, *([fake] * 4), *args, stream=0)
+    assert st == fa.FA_ERR_INVALID_ARG and "null" in fa.fa_last_error()

@@ -14,8 +14,8 @@ import numpy as np
 import pytest
 
 from oracle import (attention_probs, attn_bwd, attn_bwd_dkdv_cols, attn_bwd_dq_rows,
-                    attn_bwd_head, attn_fwd, attn_fwd_head, attn_fwd_rows, allowed_keys,
-                    attended_pairs)
+                    attn_bwd_head, attn_bwd_varlen, attn_fwd, attn_fwd_head, attn_fwd_rows,
+                    attn_fwd_varlen, allowed_keys, attended_pairs)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
 
@@ -396,3 +396,95 @@ def test_process_pool_matches_serial():
     g2 = attn_bwd(q, k, v, do, True, 0, 0.3, workers=2)
     for a, b_ in zip(g1, g2):
         np.testing.assert_allclose(a, b_, atol=1e-14)
+
+
+# ------------------------------------------------------------------ packed sequences
+VARLEN_LENS = [5, 0, 1, 17, 9]
+
+
+def _packed(rng, lens, hq, hkv, d):
+    t = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    q = rng.standard_normal((t, hq, d))
+    k = rng.standard_normal((t, hkv, d))
+    v = rng.standard_normal((t, hkv, d))
+    do = rng.standard_normal((t, hq, d))
+    return cu, q, k, v, do
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 3), (False, 4)])
+def test_varlen_matches_torch_block_diagonal_mask(causal, window):
+    """Packed sequences = one attention over all rows with a block-diagonal mask (masks
+    counted inside each block), evaluated by torch's float64 SDPA and autograd."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(21)
+    hq, hkv, d = 4, 2, 8
+    cu, q, k, v, do = _packed(rng, VARLEN_LENS, hq, hkv, d)
+    scale = 0.4
+    o, lse = attn_fwd_varlen(q, k, v, cu, causal, window, scale)
+    dq, dk, dv, dvec = attn_bwd_varlen(q, k, v, do, cu, causal, window, scale)
+    t = q.shape[0]
+    seq = np.repeat(np.arange(len(VARLEN_LENS)), VARLEN_LENS)
+    pos = np.arange(t) - cu[seq]
+    same = seq[:, None] == seq[None, :]
+    i, j = pos[:, None], pos[None, :]
+    ok = same.copy()
+    if causal:
+        ok &= j <= i
+    if window:
+        ok &= j >= i - window + 1
+    mask = torch.tensor(ok)
+    g = hq // hkv
+    tq = torch.tensor(q).transpose(0, 1)[None].requires_grad_()
+    tk = torch.tensor(k).transpose(0, 1)[None].requires_grad_()
+    tv = torch.tensor(v).transpose(0, 1)[None].requires_grad_()
+    to = F.scaled_dot_product_attention(tq, tk.repeat_interleave(g, dim=1),
+                                        tv.repeat_interleave(g, dim=1), attn_mask=mask,
+                                        scale=scale)
+    to.backward(torch.tensor(do).transpose(0, 1)[None])
+    np.testing.assert_allclose(o, to.detach()[0].transpose(0, 1).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad[0].transpose(0, 1).numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad[0].transpose(0, 1).numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad[0].transpose(0, 1).numpy(), atol=1e-11)
+    s_ = torch.einsum("hnd,hmd->hnm", torch.tensor(q).transpose(0, 1),
+                      torch.tensor(k).transpose(0, 1).repeat_interleave(g, dim=0)) * scale
+    s_ = s_.masked_fill(~mask, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s_, dim=-1).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dvec, np.einsum("thd,thd->ht", do, o), atol=1e-12)
+
+
+def test_varlen_equal_lengths_equal_a_batch():
+    rng = np.random.default_rng(22)
+    n, nb, hq, hkv, d = 13, 3, 2, 1, 4
+    cu, q, k, v, do = _packed(rng, [n] * nb, hq, hkv, d)
+    o, lse = attn_fwd_varlen(q, k, v, cu, True, 5, 0.6)
+    ob, lseb = attn_fwd(q.reshape(nb, n, hq, d), k.reshape(nb, n, hkv, d),
+                        v.reshape(nb, n, hkv, d), True, 5, 0.6)
+    np.testing.assert_array_equal(o, ob.reshape(nb * n, hq, d))
+    np.testing.assert_array_equal(lse, lseb.transpose(1, 0, 2).reshape(hq, nb * n))
+    g = attn_bwd_varlen(q, k, v, do, cu, True, 5, 0.6)
+    gb = attn_bwd(q.reshape(nb, n, hq, d), k.reshape(nb, n, hkv, d), v.reshape(nb, n, hkv, d),
+                  do.reshape(nb, n, hq, d), True, 5, 0.6)
+    for a, bt in zip(g[:3], gb[:3]):
+        np.testing.assert_array_equal(a, bt.reshape(a.shape))
+
+
+def test_varlen_sequences_are_independent():
+    rng = np.random.default_rng(23)
+    cu, q, k, v, do = _packed(rng, [6, 7], 2, 2, 4)
+    o1, l1 = attn_fwd_varlen(q, k, v, cu, False, 0, 0.5)
+    k2 = k.copy()
+    k2[:6] += rng.standard_normal(k2[:6].shape)  # change only the first sequence's keys
+    o2, l2 = attn_fwd_varlen(q, k2, v, cu, False, 0, 0.5)
+    np.testing.assert_array_equal(o1[6:], o2[6:])
+    np.testing.assert_array_equal(l1[:, 6:], l2[:, 6:])
+    assert np.abs(o1[:6] - o2[:6]).max() > 1e-6
+
+
+def test_varlen_rejects_bad_offsets():
+    rng = np.random.default_rng(24)
+    cu, q, k, v, _ = _packed(rng, [3, 4], 1, 1, 2)
+    for bad in ([1, 3, 7], [0, 5, 4], [0, 3, 6]):
+        with pytest.raises(ValueError):
+            attn_fwd_varlen(q, k, v, bad)
