@@ -4,7 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 A step is one forward (fa_fwd) and one backward (fa_bwd) over one batch of the workload,
-with every input already resident in device memory.  The timed region is bracketed by
+with every input already resident in device memory; a packed-sequence workload
+(--workload bf16_varlen_...) runs fa_fwd_varlen / fa_bwd_varlen instead and sums the FLOPs
+over its sequences.  The timed region is bracketed by
 torch.cuda.synchronize(); per-launch kernel durations come from HIP events recorded on the
 stream the kernels run on.  Prints ONE JSON line.
 
@@ -94,10 +96,38 @@ def mfma_probe(fa, torch, dev, stream, blocks: int = 2048, iters: int = 20000, r
     return flop / (best * 1e-3) / 1e12
 
 
-def cpu_baseline(w, q, k, v, do, max_workers: int = 16):
-    """Time the float64 oracle on a bounded sample of (batch, head) pairs of the same
-    inputs on the host cores; report algorithmic TFLOP/s with the same FLOP convention."""
+def _head_tasks(w, q, k, v, do, packed):
+    """(flop, task maker) per (batch entry or sequence, query head), in an order that
+    spreads a prefix over every sequence length: head-major for packed batches."""
     import numpy as np
+    import oracle.attention as oa
+
+    g = w.Hq // w.Hkv
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    if packed:
+        cu = w.cu_seqlens
+        slots = [(h, s) for h in range(w.Hq) for s in range(len(w.lengths)) if w.lengths[s]]
+        for h, s in slots:
+            a, n = cu[s], w.lengths[s]
+            flop = 4.0 * attended_pairs(n, w.causal, w.window) * w.d
+            yield flop, lambda a=a, n=n, h=h: (
+                f64(q[a:a + n, h]), f64(k[a:a + n, h // g]), f64(v[a:a + n, h // g]),
+                None if do is None else f64(do[a:a + n, h]), w.causal, w.window, w.scale,
+                oa.DEFAULT_ROW_CHUNK)
+    else:
+        flop = 4.0 * attended_pairs(w.N, w.causal, w.window) * w.d
+        for i in range(w.B * w.Hq):
+            b, h = i // w.Hq, i % w.Hq
+            yield flop, lambda b=b, h=h: (
+                f64(q[b, :, h]), f64(k[b, :, h // g]), f64(v[b, :, h // g]),
+                None if do is None else f64(do[b, :, h]), w.causal, w.window, w.scale,
+                oa.DEFAULT_ROW_CHUNK)
+
+
+def cpu_baseline(w, q, k, v, do, packed=False, max_workers: int = 16):
+    """Time the float64 oracle on a bounded sample of (batch entry or sequence, head) pairs
+    of the same inputs on the host cores; report algorithmic TFLOP/s with the same FLOP
+    convention."""
     from concurrent.futures import ProcessPoolExecutor
     import multiprocessing as mp
     import oracle.attention as oa
@@ -107,42 +137,34 @@ def cpu_baseline(w, q, k, v, do, max_workers: int = 16):
     except AttributeError:
         cores = os.cpu_count() or 1
     workers = max(1, min(max_workers, cores))
-    per_head_f = fwd_flops(w) / (w.B * w.Hq)
     bwd = do is not None
+    mult = 3.5 if bwd else 1.0
     # about 20 s of wall time at ~25 GFLOP/s per float64 worker, at most the whole workload
-    est_head_s = per_head_f * (3.5 if bwd else 1.0) / 25e9
-    n_heads = min(w.B * w.Hq, max(workers, int(20.0 * workers / max(est_head_s, 1e-3))))
-    g = w.Hq // w.Hkv
-    pairs = [(i // w.Hq, i % w.Hq) for i in range(n_heads)]
-    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
-    tasks = []
-    for b, h in pairs:
-        qh, kh, vh = f64(q[b, :, h]), f64(k[b, :, h // g]), f64(v[b, :, h // g])
-        if bwd:
-            tasks.append((qh, kh, vh, f64(do[b, :, h]), w.causal, w.window, w.scale,
-                          oa.DEFAULT_ROW_CHUNK))
-        else:
-            tasks.append((qh, kh, vh, w.causal, w.window, w.scale, oa.DEFAULT_ROW_CHUNK))
+    budget = 20.0 * workers * 25e9
+    tasks, flop, n_all = [], 0.0, 0
+    for f, t in _head_tasks(w, q, k, v, do, packed):
+        n_all += 1
+        if len(tasks) >= workers and flop >= budget:
+            continue
+        tasks.append(t())
+        flop += f * mult
     ctx = mp.get_context("spawn")
     with ProcessPoolExecutor(max_workers=workers, mp_context=ctx,
                              initializer=oa._limit_blas_threads) as ex:
         # start every worker before the clock runs
         list(ex.map(oa.default_workers, range(workers)))
         t0 = time.perf_counter()
+        list(ex.map(oa._fwd_task, [t[:3] + t[4:] for t in tasks]))
         if bwd:
-            fwd_tasks = [t[:3] + t[4:] for t in tasks]
-            list(ex.map(oa._fwd_task, fwd_tasks))
             list(ex.map(oa._bwd_task, tasks))
-        else:
-            list(ex.map(oa._fwd_task, tasks))
         dt = time.perf_counter() - t0
-    flop = per_head_f * n_heads * (3.5 if bwd else 1.0)
+    what = "(sequence, head)" if packed else "(batch, head)"
     return {
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s (fwd+bwd, algorithmic)" if bwd else "TFLOP/s (fwd, algorithmic)",
         "cores": workers,
         "kind": "oracle",
-        "sample": f"{n_heads} of {w.B * w.Hq} (batch, head) pairs of {w.name}, "
+        "sample": f"{len(tasks)} of {n_all} {what} pairs of {w.name}, "
                   f"{'forward + backward' if bwd else 'forward'}, float64 NumPy, "
                   f"{workers} worker processes x 1 BLAS thread, {dt:.1f} s wall",
         "seconds": dt,
@@ -169,31 +191,59 @@ def main() -> int:
 
     import torch
     from exact_io_aware_fa2_amd import fa
-    from exact_io_aware_fa2_amd.workloads import HEADLINE, WORKLOADS, make_inputs
+    from exact_io_aware_fa2_amd.workloads import (HEADLINE, VARLEN_WORKLOADS, WORKLOADS,
+                                                  make_inputs, make_varlen_inputs)
 
-    w = WORKLOADS[args.workload or HEADLINE]
+    name = args.workload or HEADLINE
+    packed = name in VARLEN_WORKLOADS
+    w = VARLEN_WORKLOADS[name] if packed else WORKLOADS[name]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    q, k, v, do = make_inputs(w, dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    if packed:
+        q, k, v, do = make_varlen_inputs(w, dev)
+        cu = torch.tensor(w.cu_seqlens, dtype=torch.int32, device=dev)
+        S, T, M = len(w.lengths), w.total, w.max_seqlen
+        lse = torch.empty((w.Hq, T), device=dev, dtype=torch.float32)
+        F = sum(4.0 * w.Hq * attended_pairs(n, w.causal, w.window) * w.d for n in w.lengths)
+        config = {"workload": w.name, "num_seqs": S, "total": T, "max_seqlen": M,
+                  "lengths": list(w.lengths), "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
+                  "causal": w.causal, "window": w.window, "scale": w.scale}
+    else:
+        q, k, v, do = make_inputs(w, dev)
+        lse = torch.empty((w.B, w.Hq, w.N), device=dev, dtype=torch.float32)
+        F = fwd_flops(w)
+        config = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                  "causal": w.causal, "window": w.window, "scale": w.scale}
     o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.Hq, w.N), device=dev, dtype=torch.float32)
     bwd = do is not None and w.dtype == "bf16"
     if bwd:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = fa.workspace_for(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, dev)
+        if packed:
+            ws = fa.workspace_for_varlen(T, w.Hq, w.Hkv, w.d, dev)
+        else:
+            ws = fa.workspace_for(w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, dev)
         ws_bytes = ws.numel()
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
     fwd_fn = fa.fa_fwd if w.dtype == "bf16" else fa.fa_fwd_fp32
 
     def run_fwd():
-        st = fwd_fn(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window, w.scale, sh)
+        if packed:
+            st = fa.fa_fwd_varlen(q, k, v, o, lse, cu, S, T, M, w.Hq, w.Hkv, w.d, w.causal,
+                                  w.window, w.scale, sh)
+        else:
+            st = fwd_fn(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
+                        w.scale, sh)
         if st != fa.FA_OK:
             raise RuntimeError(fa.fa_last_error())
 
     def run_bwd():
-        st = fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal,
-                       w.window, w.scale, ws, ws_bytes, sh)
+        if packed:
+            st = fa.fa_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, cu, S, T, M, w.Hq, w.Hkv,
+                                  w.d, w.causal, w.window, w.scale, ws, ws_bytes, sh)
+        else:
+            st = fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.B, w.Hq, w.Hkv, w.N, w.d,
+                           w.causal, w.window, w.scale, ws, ws_bytes, sh)
         if st != fa.FA_OK:
             raise RuntimeError(fa.fa_last_error())
 
@@ -225,7 +275,6 @@ def main() -> int:
 
     fwd_ms = [e[0].elapsed_time(e[1]) for e in ev]
     ms_step = wall * 1e3 / K
-    F = fwd_flops(w)
     total_flop = F * (3.5 if bwd else 1.0)
     out = {
         "metric": "attention fwd & fwd+bwd TFLOPs/s (bf16, d=128, N=8K causal); % of MFMA peak",
@@ -240,8 +289,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0, sigma^2) draws, rounded to the compute dtype)",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "window": w.window, "scale": w.scale},
+        "config": config,
     }
     avg = lambda xs: sum(xs) / len(xs)  # noqa: E731
     fwd_avg = avg(fwd_ms)
@@ -304,7 +352,7 @@ def main() -> int:
     out["context"] = ("pages' A100 figures at 16K tokens (other hardware, not a target): "
                       "~50 TFLOP/s standard PyTorch attention vs >180 TFLOP/s FlashAttention-2")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do if bwd else None)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do if bwd else None, packed)
     print(json.dumps(out), flush=True)
     return 0
 

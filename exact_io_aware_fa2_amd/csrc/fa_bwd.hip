@@ -16,10 +16,13 @@
 // query-block kernel costs two extra products per tile pair but removes the float32 dQ
 // accumulator, its atomics and its conversion pass, and keeps dQ deterministic.
 //
-// Key-block kernel: a workgroup = 4 waves = 128 keys of one (batch, KV head) (32 keys per
-// wave; for d = 256 one half of the head dim of dK/dV).  The wave's K and V rows are MFMA B
-// operands in VGPRs; dK^T and dV^T accumulate in registers across every query head of the
-// GQA group and every query block, and are written once.
+// Key-block kernel: a workgroup = 8 waves = 256 keys of one (batch entry, KV head) for
+// d <= 128 (bwd_dkdv8_kernel), 4 waves = 128 keys and one half of the head dim of dK/dV for
+// d = 256 (bwd_dkdv_kernel); 32 keys per wave.  The wave's K rows are MFMA B operands in
+// VGPRs; dK^T and dV^T accumulate in registers across every query head of the GQA group
+// and every query block, and are written once.
+//
+// Both grids follow work_item: each XCD owns a range of heads, heaviest blocks first.
 //
 // Query-block kernel: a workgroup = 8 waves (d <= 128) or 4 waves = 32 query rows per wave,
 // the same shape as the forward: Q and dO rows are B operands in VGPRs, K, V and K^T tiles
@@ -72,6 +75,16 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16_t* __restrict__
   }
 }
 
+// Key block of a given cost rank (0 = heaviest) in a sequence of `nb` key blocks, when the
+// longest sequence has `num_kb`.  Causal or unmasked: a block's cost is the number of query
+// rows that reach it, which falls towards the end of the sequence, so the ranks count blocks
+// from the sequence's end and rank 0 is block 0 of the longest sequences only.  A pure left
+// window: later blocks are reached by more rows, so the ranks count down from the last
+// block.  Ranks with no block in a shorter sequence give a negative or too-large index.
+__device__ __forceinline__ int key_block(int rank, int num_kb, int nb, int causal, int window) {
+  return (!causal && window > 0) ? num_kb - 1 - rank : nb - num_kb + rank;
+}
+
 // =====================================================================================
 // dK / dV
 template <int D>
@@ -105,18 +118,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int num_kb = (Nmax + BKN - 1) / BKN;
-  const int total = B * Hkv * num_kb * NSPLIT;
-  const int lin = xcd_remap(blockIdx.x, total);
-  const int split = lin % NSPLIT;
-  const int t1 = lin / NSPLIT;
-  const int head = t1 / num_kb;
-  const int kbo = t1 - head * num_kb;
-  // longest first: causal -> low key blocks see the most rows; a pure left window -> high.
-  const int kb = (!causal && window > 0) ? num_kb - 1 - kbo : kbo;
-  const int b = head / Hkv, hkv = head - b * Hkv;
+  // the head-dim splits of one key block are adjacent ranks of equal cost
+  int b, hkv, rs;
+  work_item(B, Hkv, num_kb * NSPLIT, b, hkv, rs);
+  const int split = rs % NSPLIT, rank = rs / NSPLIT;
   int seq0, N;  // first row and length of this batch entry's sequence
   seq_span(cu, ntot, b, Nmax, seq0, N);
-  if (kb * BKN >= N) return;  // a key block past the end of a shorter packed sequence
+  const int kb = key_block(rank, num_kb, (N + BKN - 1) / BKN, causal, window);
+  if (kb < 0 || kb * BKN >= N) return;  // no such block in a shorter packed sequence
   const int G = Hq / Hkv;
   const int dh0 = split * DH;
 
@@ -382,15 +391,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   char* stage = smem + Cfg::SV * 2;
 
   const int num_kb = (Nmax + BKN - 1) / BKN;
-  const int total = B * Hkv * num_kb;
-  const int lin = xcd_remap(blockIdx.x, total);
-  const int head = lin / num_kb;
-  const int kbo = lin - head * num_kb;
-  const int kb = (!causal && window > 0) ? num_kb - 1 - kbo : kbo;  // longest first
-  const int b = head / Hkv, hkv = head - b * Hkv;
+  int b, hkv, rank;
+  work_item(B, Hkv, num_kb, b, hkv, rank);
   int seq0, N;  // first row and length of this batch entry's sequence
   seq_span(cu, ntot, b, Nmax, seq0, N);
-  if (kb * BKN >= N) return;  // a key block past the end of a shorter packed sequence
+  const int kb = key_block(rank, num_kb, (N + BKN - 1) / BKN, causal, window);
+  if (kb < 0 || kb * BKN >= N) return;  // no such block in a shorter packed sequence
   const int G = Hq / Hkv;
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
@@ -635,11 +641,9 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
 
   const int num_m = (Nmax + BM - 1) / BM;
-  const int total = B * Hq * num_m;
-  const int lin = xcd_remap(blockIdx.x, total);
-  const int head = lin / num_m;
-  const int mb = num_m - 1 - (lin - head * num_m);
-  const int b = head / Hq, hq = head - b * Hq;
+  int b, hq, rank;
+  work_item(B, Hq, num_m, b, hq, rank);
+  const int mb = num_m - 1 - rank;  // causal: the last row block attends the most keys
   const int hkv = hq / (Hq / Hkv);
   int seq0, N;  // first row and length of this batch entry's sequence
   seq_span(cu, ntot, b, Nmax, seq0, N);

@@ -216,17 +216,31 @@ __device__ __forceinline__ void store_4x8_transposed(bf16_t* lds, int ts, int lr
   }
 }
 
-// Blocks are dispatched round-robin over the 8 XCDs (each with its own L2).  Map the
-// hardware block id so that consecutive logical ids land on the same XCD: XCD x runs the
-// logical ids [x * T / 8, (x + 1) * T / 8) in order.  A bijection for any T.
-__device__ __forceinline__ int xcd_remap(int hw, int total) {
+// Work order over (batch entry, head, block) triples; `rank` 0 is the heaviest block of a
+// head.  Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  When
+// H is a multiple of 8, XCD x owns the heads [x H/8, (x+1) H/8) of every batch entry (a GQA
+// group, which shares K and V, stays on one L2) and runs its blocks rank-major: every owned
+// head's heaviest block first, then the next rank.  Over the whole chip the heaviest blocks
+// start first, which keeps the tail short, also when packed sequences of very different
+// lengths make the batch entries unequal.  Other H: plain rank-major order.
+__device__ __forceinline__ void work_item(int B, int H, int nblocks, int& b, int& h,
+                                          int& rank) {
   constexpr int kXcd = 8;
-  const int per = total / kXcd, rem = total % kXcd;
-  const int xcd = hw % kXcd, slot = hw / kXcd;
-  if (per == 0) return hw;
-  // XCDs [0, rem) receive per + 1 blocks, the others per blocks.
-  if (slot >= per + (xcd < rem ? 1 : 0)) return hw;  // unreachable for a full grid
-  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int id = blockIdx.x;
+  if (H % kXcd == 0) {
+    const int hc = H / kXcd, hpx = B * hc;  // heads per XCD
+    const int xcd = id % kXcd, slot = id / kXcd;
+    rank = slot / hpx;
+    const int j = slot - rank * hpx;
+    b = j / hc;
+    h = xcd * hc + (j - b * hc);
+  } else {
+    const int nh = B * H;
+    rank = id / nh;
+    const int head = id - rank * nh;
+    b = head / H;
+    h = head - b * H;
+  }
 }
 
 }  // namespace fa

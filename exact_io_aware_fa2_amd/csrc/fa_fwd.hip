@@ -6,22 +6,22 @@
 // denominator kept apart and combined once at the end; section 3.2: the Q tile stays in
 // registers while K and V tiles go through shared memory).
 //
-// bf16 kernel, one workgroup = 4 waves = 128 query rows of one (batch, query head):
+// bf16 kernel, one workgroup = 8 waves = 256 query rows (d <= 128; 4 waves = 128 rows for
+// d = 256) of one (batch entry, query head):
 //   * each wave owns 32 query rows; its Q rows sit in VGPRs as the B operand of
 //     S^T = K Q^T (32 keys x 32 rows per MFMA tile), so every lane holds one query row
 //     and 16 of its scores per tile -> row max/sum need one cross-half exchange only;
-//   * K and V tiles of 64 keys are staged in LDS (row stride d + 8 elements) from
-//     16-byte coalesced global loads, with the next tile's loads in flight during the
-//     current tile's math;
+//   * K and V tiles (64 keys for d <= 128) are staged in LDS, double-buffered, from
+//     16-byte raw buffer loads issued one tile ahead; V is transposed on the way in
+//     (v_perm_b32 on register pairs), so V^T rows are plain 16-byte LDS reads;
 //   * P^T (the accumulator of S^T after exp2) feeds O^T += V^T P^T directly as the B
-//     operand; V^T comes from LDS with the transposing ds_read_b64_tr_b16;
+//     operand;
 //   * scores are handled in log2 units: t = (q.k) * |scale| * log2(e), so each probability
 //     is one FMA and one exp2; a negative scale is handled by negating Q exactly;
 //   * key tiles outside the causal / sliding-window band are never visited, and only
 //     tiles crossing the band edge (or the end of the sequence) pay for per-element masks
 //     (bmjup.com page, section 3.3: tile-level encoding of the mask);
-//   * grid: (batch, head) major, longest query tiles first inside a head, block ids
-//     remapped so that all tiles of a head run on one XCD and share its L2.
+//   * grid: each XCD owns a range of heads (work_item), heaviest query blocks first.
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
@@ -73,11 +73,9 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
 
   const int num_m = (Nmax + BM - 1) / BM;
-  const int total = B * Hq * num_m;
-  const int lin = xcd_remap(blockIdx.x, total);
-  const int head = lin / num_m;
-  const int mb = num_m - 1 - (lin - head * num_m);
-  const int b = head / Hq, hq = head - b * Hq;
+  int b, hq, rank;
+  work_item(B, Hq, num_m, b, hq, rank);
+  const int mb = num_m - 1 - rank;  // causal: the last row block attends the most keys
   const int hkv = hq / (Hq / Hkv);
   int seq0, N;  // first row and length of this batch entry's sequence
   seq_span(cu, ntot, b, Nmax, seq0, N);

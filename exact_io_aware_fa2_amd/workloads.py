@@ -122,6 +122,7 @@ class VarlenWorkload:
     causal: bool
     window: int = 0
     seed: int = 2000
+    dtype: str = "bf16"
 
     @property
     def total(self) -> int:
