@@ -67,7 +67,15 @@ WORKLOADS = {
 
 HEADLINE = "bf16_b2_h32_n8192_d128_causal"
 
+# The bench workload's shape with 8-bit E4M3 inputs (forward only).
+FP8_WORKLOADS = {
+    "fp8_b2_h32_n8192_d128_causal": Workload("fp8_b2_h32_n8192_d128_causal", "fp8", 2, 32, 32,
+                                             8192, 128, True, backward=False, seed=1006),
+}
+
 _TORCH_DTYPE = {"fp32": torch.float32, "bf16": torch.bfloat16}
+
+E4M3_MAX = 448.0
 
 
 def torch_dtype(w: Workload) -> torch.dtype:
@@ -182,3 +190,31 @@ def make_varlen_inputs(w: VarlenWorkload, device: str | torch.device = "cpu"):
     v = draw(w.Hkv)
     do = draw(w.Hq)
     return q, k, v, do
+
+
+# ------------------------------------------------------------------ 8-bit inputs
+def quantize_e4m3(x: torch.Tensor):
+    """Per-tensor scaling into the E4M3 range: factor = amax / 448 in float32, codes = the
+    round-to-nearest-even E4M3 cast of x / factor (torch's float8_e4m3fn conversion).
+    Returns (codes as a uint8 tensor, factor); factor * decoded code approximates x."""
+    amax = float(x.abs().max())
+    factor = float(torch.tensor(amax / E4M3_MAX if amax > 0 else 1.0, dtype=torch.float32))
+    y = (x.float() / factor).clamp_(-E4M3_MAX, E4M3_MAX)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8), factor
+
+
+def make_fp8_inputs(w: Workload, device: str | torch.device = "cpu"):
+    """(q8, k8, v8, (fq, fk, fv)) for a forward-only workload: float32 draws in the order
+    and manner of make_inputs (before any rounding), each quantized per tensor."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+    out, factors = [], []
+    for shape, sigma in (((w.B, w.N, w.Hq, w.d), w.sigma_q), ((w.B, w.N, w.Hkv, w.d), w.sigma_k),
+                         ((w.B, w.N, w.Hkv, w.d), w.sigma_v)):
+        x = torch.randn(shape, generator=g, dtype=torch.float32)
+        if sigma != 1.0:
+            x.mul_(sigma)
+        c, f = quantize_e4m3(x)
+        out.append(c.to(device))
+        factors.append(f)
+    return out[0], out[1], out[2], tuple(factors)

@@ -21,6 +21,9 @@ rescaling.  Sources (the pages this build follows):
 * hysenlabs.com, "dao-ailab flash-attention", hardware-boundary section: MQA/GQA
   (KV heads shared by groups of query heads).
 
+``oracle.fp8`` adds the 8-bit floating-point forward: the same definition on inputs
+decoded from E4M3 codes and multiplied by per-tensor factors.
+
 The backward pass is the analytic derivative of the forward (the pages only say
 the matrix is recomputed); it is written as the softmax Jacobian-vector product.
 """
@@ -28,6 +31,7 @@ the matrix is recomputed); it is written as the softmax Jacobian-vector product.
 from .attention import (  # noqa: F401
     allowed_keys,
     attention_probs,
+    attention_probs_rows,
     attn_fwd_head,
     attn_bwd_head,
     attn_fwd,
@@ -39,3 +43,4 @@ from .attention import (  # noqa: F401
     attn_fwd_varlen,
     attn_bwd_varlen,
 )
+from .fp8 import attn_fwd_fp8, attn_fwd_fp8_rows, dequantize, e4m3_decode  # noqa: F401

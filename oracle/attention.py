@@ -116,6 +116,20 @@ def attention_probs(q, k, causal=False, window=0, scale=None) -> np.ndarray:
     return full
 
 
+def attention_probs_rows(q, k, rows, causal=False, window=0, scale=None) -> np.ndarray:
+    """Rows ``rows`` of the probability matrix P of one head, full width [len(rows), Nk]."""
+    q = _as64(q)
+    k = _as64(k)
+    scale = 1.0 / math.sqrt(q.shape[1]) if scale is None else float(scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, k.shape[0]))
+    for a in range(0, rows.size, 64):
+        rr = rows[a:a + 64]
+        p, _, lo, hi = _probs_rows(q, k, rr, causal, window, scale)
+        out[a:a + 64, lo:hi] = p
+    return out
+
+
 def attn_fwd_rows(q, k, v, rows, causal=False, window=0, scale=None):
     """O and LSE of one head for the selected query ``rows`` only.
 

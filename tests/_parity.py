@@ -6,6 +6,14 @@ Tolerances (bf16 inputs, float32 accumulation):
   LSE  : max |LSE - LSE_ref| <= 1e-3
   dQ/dK/dV : ||X - X_ref||_F / ||X_ref||_F <= 3e-2 per tensor
 float32 inputs: ||O - O_ref||_F / ||O_ref||_F <= 1e-5, |LSE - LSE_ref| <= 1e-5 max(1, |LSE_ref|).
+E4M3 inputs (the fp8 forward): the kernel rounds each probability weight to E4M3 before the
+second product and normalises by the unrounded weight sum.  With w_j = P_ij / max_j P_ij
+the rounded weight is off by at most max(2^-4 w_j, 2^-10) (round to nearest: 3 mantissa
+bits; below 2^-6 the subnormal spacing 2^-9, at any reference at or below the row max),
+masked keys exactly 0.  Hence, per output element,
+  |O_ic - O_ref_ic| <= 1.02 sum_j max(2^-4 P_ij, 2^-10 max_j P_ij) |v_jc| + 2^-8 |O_ref_ic|
+(1.02 covers float32 score, exp and sum errors; 2^-8 the bf16 rounding of O), and LSE,
+taken from unrounded weights, keeps the bf16 tolerance.
 """
 
 from __future__ import annotations
@@ -78,3 +86,19 @@ def gpu_bwd(q, k, v, o, do, lse, causal, window, scale, return_ws=False):
     if return_ws:
         return dq, dk, dv, ws
     return dq, dk, dv
+
+
+def fp8_o_bound(p: np.ndarray, v: np.ndarray, o_ref: np.ndarray) -> np.ndarray:
+    """Elementwise bound on |O - O_ref| for the fp8 forward of one head: p [rows, Nk] the
+    oracle's probabilities of those rows, v [Nk, dv] the dequantised values, o_ref [rows, dv]."""
+    pmax = p.max(axis=1, keepdims=True)
+    delta = np.where(p > 0, np.maximum(2.0 ** -4 * p, 2.0 ** -10 * pmax), 0.0)
+    return 1.02 * (delta @ np.abs(v)) + 2.0 ** -8 * np.abs(o_ref) + 1e-6
+
+
+def check_fp8_o(o: np.ndarray, o_ref: np.ndarray, bound: np.ndarray, what: str = "O"):
+    err = np.abs(o - o_ref)
+    assert np.isfinite(o).all(), f"{what}: non-finite output"
+    worst = float((err / bound).max())
+    assert worst <= 1.0, f"{what}: error reaches {worst:.2f} x the fp8 rounding bound"
+    return worst

@@ -13,7 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (attention_probs, attn_bwd, attn_bwd_dkdv_cols, attn_bwd_dq_rows,
+from oracle import (attention_probs, attention_probs_rows, attn_fwd_fp8, e4m3_decode, attn_bwd, attn_bwd_dkdv_cols, attn_bwd_dq_rows,
                     attn_bwd_head, attn_bwd_varlen, attn_fwd, attn_fwd_head, attn_fwd_rows,
                     attn_fwd_varlen, allowed_keys, attended_pairs)
 
@@ -488,3 +488,101 @@ def test_varlen_rejects_bad_offsets():
     for bad in ([1, 3, 7], [0, 5, 4], [0, 3, 6]):
         with pytest.raises(ValueError):
             attn_fwd_varlen(q, k, v, bad)
+
+
+# ------------------------------------------------------------------ 8-bit inputs
+def test_attention_probs_rows_match_full_matrix():
+    rng = np.random.default_rng(40)
+    q, k = rng.standard_normal((37, 8)), rng.standard_normal((37, 8))
+    rows = np.array([0, 5, 36, 17])
+    for causal, window in [(False, 0), (True, 0), (True, 6), (False, 9)]:
+        full = attention_probs(q, k, causal, window, 0.3)
+        np.testing.assert_array_equal(attention_probs_rows(q, k, rows, causal, window, 0.3),
+                                      full[rows])
+
+
+def test_e4m3_decode_matches_torch_on_every_code():
+    torch = pytest.importorskip("torch")
+    codes = np.arange(256, dtype=np.uint8)
+    ours = e4m3_decode(codes)
+    ref = torch.tensor(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[ok], ref[ok])
+    assert np.isnan(ours).sum() == 2  # 0x7F and 0xFF only
+
+
+def test_e4m3_decode_closed_forms():
+    # bias 7, 3 mantissa bits, subnormals below 2^-6, no infinities
+    cases = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0x78: 256.0, 0xB8: -1.0, 0xFE: -448.0}
+    for c, val in cases.items():
+        assert e4m3_decode(np.array([c], np.uint8))[0] == val, hex(c)
+    assert np.signbit(e4m3_decode(np.array([0x80], np.uint8))[0])
+
+
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 5)])
+def test_attn_fwd_fp8_is_attention_of_dequantized_inputs(causal, window):
+    """Against torch's float8 decode and float64 SDPA (an independent path)."""
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(41)
+    b, n, hq, hkv, d = 2, 19, 4, 2, 16
+    codes = [rng.integers(0, 256, size=(b, n, h, d), dtype=np.uint8) for h in (hq, hkv, hkv)]
+    codes = [np.where((c & 0x7F) == 0x7F, 0x3A, c).astype(np.uint8) for c in codes]  # no NaN
+    f = (0.02, 0.011, 0.5)
+    o, lse = attn_fwd_fp8(*codes, *f, causal, window, 0.25)
+    t = [torch.tensor(c).view(torch.float8_e4m3fn).double() * fi for c, fi in zip(codes, f)]
+    g = hq // hkv
+    tq = t[0].transpose(1, 2)
+    tk = t[1].transpose(1, 2).repeat_interleave(g, dim=1)
+    tv = t[2].transpose(1, 2).repeat_interleave(g, dim=1)
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    ok = torch.ones(n, n, dtype=torch.bool)
+    if causal:
+        ok &= j <= i
+    if window:
+        ok &= j >= i - window + 1
+    ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=ok, scale=0.25)
+    np.testing.assert_allclose(o, ref.transpose(1, 2).numpy(), rtol=1e-12, atol=1e-12)
+    s = (tq @ tk.transpose(-1, -2) * 0.25).masked_fill(~ok, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("offset", [0.0, 1.3, 3.0])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 7)])
+def test_fp8_error_bound_holds_for_e4m3_rounded_weights(offset, causal, window):
+    """The per-element bound the fp8 GPU tests use, checked against weights rounded to E4M3
+    by torch (round to nearest even) at a reference `offset` log2 units below the row max,
+    normalised by the unrounded sum."""
+    torch = pytest.importorskip("torch")
+    from tests._parity import fp8_o_bound
+    rng = np.random.default_rng(42)
+    n, d = 300, 32
+    q = rng.standard_normal((n, d)) * 2.0
+    k = rng.standard_normal((n, d))
+    v = rng.standard_normal((n, d))
+    p = attention_probs(q, k, causal, window, 0.3)
+    o_ref = p @ v
+    w = p / p.max(axis=1, keepdims=True) * 2.0 ** offset
+    wr = torch.tensor(w).float().to(torch.float8_e4m3fn).double().numpy()
+    o_emul = (wr @ v) / w.sum(axis=1, keepdims=True)
+    bound = fp8_o_bound(p, v, o_ref)
+    err = np.abs(o_emul - o_ref)
+    assert (err <= bound).all(), float((err / bound).max())
+    assert (err / bound).max() > 0.02  # the bound is not vacuous for this data
+
+
+def test_quantize_e4m3_roundtrip():
+    torch = pytest.importorskip("torch")
+    from exact_io_aware_fa2_amd.workloads import quantize_e4m3
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(4000, generator=g) * 3.0
+    codes, f = quantize_e4m3(x)
+    y = e4m3_decode(codes.numpy()) * f
+    assert np.abs(y).max() == pytest.approx(float(x.abs().max()), rel=2 ** -4)
+    xs = x.double().numpy()
+    normal = np.abs(xs) >= 2.0 ** -6 * f
+    assert (np.abs(y - xs)[normal] <= 2.0 ** -4 * np.abs(xs)[normal] * (1 + 1e-6)).all()
+    assert (np.abs(y - xs)[~normal] <= 2.0 ** -10 * f * (1 + 1e-6)).all()
