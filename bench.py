@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak (256 CU x 2.4 GHz x 4096)
+MFMA_FP8_PEAK_TFLOPS = 5033.2   # MI355X dense fp8 matrix peak (twice the bf16 rate)
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -191,12 +192,14 @@ def main() -> int:
 
     import torch
     from exact_io_aware_fa2_amd import fa
-    from exact_io_aware_fa2_amd.workloads import (HEADLINE, VARLEN_WORKLOADS, WORKLOADS,
-                                                  make_inputs, make_varlen_inputs)
+    from exact_io_aware_fa2_amd.workloads import (FP8_WORKLOADS, HEADLINE, VARLEN_WORKLOADS,
+                                                  WORKLOADS, make_fp8_inputs, make_inputs,
+                                                  make_varlen_inputs)
 
     name = args.workload or HEADLINE
     packed = name in VARLEN_WORKLOADS
-    w = VARLEN_WORKLOADS[name] if packed else WORKLOADS[name]
+    fp8 = name in FP8_WORKLOADS
+    w = VARLEN_WORKLOADS[name] if packed else FP8_WORKLOADS[name] if fp8 else WORKLOADS[name]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -210,13 +213,21 @@ def main() -> int:
         config = {"workload": w.name, "num_seqs": S, "total": T, "max_seqlen": M,
                   "lengths": list(w.lengths), "Hq": w.Hq, "Hkv": w.Hkv, "d": w.d,
                   "causal": w.causal, "window": w.window, "scale": w.scale}
+    elif fp8:
+        q, k, v, factors = make_fp8_inputs(w, dev)
+        do = None
+        lse = torch.empty((w.B, w.Hq, w.N), device=dev, dtype=torch.float32)
+        F = fwd_flops(w)
+        config = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                  "causal": w.causal, "window": w.window, "scale": w.scale,
+                  "inputs": "E4M3 codes, one float32 factor per tensor", "descale": factors}
     else:
         q, k, v, do = make_inputs(w, dev)
         lse = torch.empty((w.B, w.Hq, w.N), device=dev, dtype=torch.float32)
         F = fwd_flops(w)
         config = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                   "causal": w.causal, "window": w.window, "scale": w.scale}
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, device=dev, dtype=torch.bfloat16) if fp8 else torch.empty_like(q)
     bwd = do is not None and w.dtype == "bf16"
     if bwd:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -231,6 +242,9 @@ def main() -> int:
         if packed:
             st = fa.fa_fwd_varlen(q, k, v, o, lse, cu, S, T, M, w.Hq, w.Hkv, w.d, w.causal,
                                   w.window, w.scale, sh)
+        elif fp8:
+            st = fa.fa_fwd_fp8(q, k, v, o, lse, *factors, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal,
+                               w.window, w.scale, sh)
         else:
             st = fwd_fn(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
                         w.scale, sh)
@@ -287,7 +301,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3"}.get(w.dtype, "f32"),
         "data": "synthetic (seeded N(0, sigma^2) draws, rounded to the compute dtype)",
         "config": config,
     }
@@ -295,8 +309,10 @@ def main() -> int:
     fwd_avg = avg(fwd_ms)
     out["fwd_ms"] = fwd_avg
     out["fwd_tflops"] = F / (fwd_avg * 1e-3) / 1e12
-    out["fwd_frac_of_peak"] = out["fwd_tflops"] / MFMA_BF16_PEAK_TFLOPS
-    kernels = {"fwd_bf16_kernel": (fwd_avg, F, "fa_fwd.hip")}
+    peak = MFMA_FP8_PEAK_TFLOPS if fp8 else MFMA_BF16_PEAK_TFLOPS
+    out["fwd_frac_of_peak"] = out["fwd_tflops"] / peak
+    kernels = ({"fwd_fp8_kernel": (fwd_avg, F, "fa_fwd_fp8.hip")} if fp8 else
+               {"fwd_bf16_kernel": (fwd_avg, F, "fa_fwd.hip")})
     if bwd:
         bwd_ms = [e[2].elapsed_time(e[3]) for e in ev]
         pre_ms = [e[2].elapsed_time(e[4]) for e in ev]   # D = rowsum(dO * O)
@@ -326,7 +342,7 @@ def main() -> int:
         out["mfma_probe_tflops"] = probe
         # the clock the probe implies: peak is 1024 flop / clock / SIMD x 1024 SIMDs
         out["mfma_probe_implied_sclk_mhz"] = probe * 1e12 / (1024 * 1024) / 1e6
-    if w.dtype == "bf16":
+    if w.dtype in ("bf16", "fp8"):
         name = max(kernels, key=lambda n: kernels[n][0])
         ms, flop, src = kernels[name]
         achieved = flop / (ms * 1e-3) / 1e12
@@ -334,9 +350,9 @@ def main() -> int:
             "kernel": name,
             "bound": "mfma",
             "achieved": achieved,
-            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+            "frac": achieved / peak,
             "traffic": _traffic(name, w.name, src),
             "avg_launch_ms": ms,
             "frac_of_measured_mfma": achieved / probe if probe else None,
@@ -352,7 +368,11 @@ def main() -> int:
     out["context"] = ("pages' A100 figures at 16K tokens (other hardware, not a target): "
                       "~50 TFLOP/s standard PyTorch attention vs >180 TFLOP/s FlashAttention-2")
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do if bwd else None, packed)
+        if fp8:  # the oracle runs on the dequantised inputs
+            deq = [t.view(torch.float8_e4m3fn).float() * f for t, f in zip((q, k, v), factors)]
+            out["cpu_baseline"] = cpu_baseline(w, *deq, None, packed)
+        else:
+            out["cpu_baseline"] = cpu_baseline(w, q, k, v, do if bwd else None, packed)
     print(json.dumps(out), flush=True)
     return 0
 

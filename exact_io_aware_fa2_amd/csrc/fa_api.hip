@@ -114,6 +114,29 @@ fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, 
   return launched("fa_fwd_fp32", fa::launch_fwd_fp32(a, (hipStream_t)stream));
 }
 
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                     float descale_q, float descale_k, float descale_v, int B, int Hq, int Hkv,
+                     int N, int d, int causal, int window, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: null pointer");
+  fa_status st = check_common("fa_fwd_fp8", B, Hq, Hkv, N, d, causal, window, scale);
+  if (st != FA_OK) return st;
+  if (!(isfinite(descale_q) && descale_q > 0.f && isfinite(descale_k) && descale_k > 0.f &&
+        isfinite(descale_v) && descale_v > 0.f))
+    return fail(FA_ERR_INVALID_ARG,
+                "fa_fwd_fp8: dequantisation factors must be finite and positive (%g, %g, %g)",
+                (double)descale_q, (double)descale_k, (double)descale_v);
+  // The kernel multiplies the raw code products by |scale| dq dk log2(e) (a negative scale
+  // negates Q exactly); a product that underflows is replaced by a tiny positive value so
+  // that masked scores stay -inf, as in fa_fwd.
+  const double cd = fabs((double)scale) * descale_q * descale_k * 1.4426950408889634;
+  if (!(cd < 3.0e38))
+    return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: |scale| * descale_q * descale_k too large");
+  const float c2 = cd < 1e-30 ? 1e-30f : (float)cd;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal ? 1 : 0, window, c2, 0.f,
+                scale < 0.f ? 1 : 0, nullptr, 0, descale_v};
+  return launched("fa_fwd_fp8", fa::launch_fwd_fp8(a, (hipStream_t)stream));
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int window) {
   if (check_common("fa_bwd_workspace_size", B, Hq, Hkv, N, d, causal, window, 1.f) != FA_OK)
     return 0;

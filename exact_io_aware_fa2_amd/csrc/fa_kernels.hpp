@@ -21,6 +21,7 @@ struct FwdArgs {
   int neg_q;            // 1 when scale < 0 (Q is negated exactly inside the kernel)
   const int* cu;        // packed sequences: B + 1 row offsets (device); null: fixed length
   int ntot;             // packed sequences: rows of the packed tensors
+  float o_scale;        // E4M3 forward: the value factor, applied to O in the epilogue
 };
 
 struct BwdArgs {
@@ -45,6 +46,7 @@ struct BwdArgs {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t st);
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
 

@@ -21,7 +21,7 @@ _lib = None
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_varlen",
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_varlen",
             "fa_bwd_varlen", "fa_bwd_varlen_workspace_size", "fa_bwd_time_main_kernel",
             "fa_mfma_probe", "fa_last_error", "fa_version")
 
@@ -50,6 +50,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = i
     lib.fa_fwd_fp32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp32.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, f, f, f, i, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
@@ -98,6 +100,13 @@ def _check(status: int):
 def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, stream=None) -> int:
     return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
                          int(causal), int(window), float(scale), _stream(stream))
+
+
+def fa_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, B, Hq, Hkv, N, d, causal,
+               window, scale, stream=None) -> int:
+    return load().fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), float(descale_q),
+                             float(descale_k), float(descale_v), B, Hq, Hkv, N, d, int(causal),
+                             int(window), float(scale), _stream(stream))
 
 
 def fa_fwd_fp32(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, stream=None) -> int:
@@ -184,6 +193,24 @@ def forward(q, k, v, causal=False, window=0, scale=None, out=None, lse=None, str
         _check(fa_fwd_fp32(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, stream))
     else:
         raise ValueError(f"unsupported dtype {q.dtype}")
+    return out, lse
+
+
+def forward_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, window=0,
+                scale=None, out=None, lse=None, stream=None):
+    """O (bf16), LSE = attention of the dequantised E4M3 inputs [B, N, H, d] (uint8 or
+    float8_e4m3fn tensors) with per-tensor factors descale_*."""
+    for t in (q8, k8, v8):
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise ValueError(f"E4M3 codes expected (uint8 or float8_e4m3fn), got {t.dtype}")
+    B, N, Hq, Hkv, d = _shapes(q8, k8, v8)
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out is None:
+        out = torch.empty((B, N, Hq, d), device=q8.device, dtype=torch.bfloat16)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), device=q8.device, dtype=torch.float32)
+    _check(fa_fwd_fp8(q8, k8, v8, out, lse, descale_q, descale_k, descale_v, B, Hq, Hkv, N, d,
+                      causal, window, scale, stream))
     return out, lse
 
 

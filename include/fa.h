@@ -67,6 +67,31 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  void* stream);
 
 /*
+ * Forward with 8-bit inputs.  The pages name an FP8 forward pass of a later version of the
+ * method (ainews.cool, "flash-attention transformer optimization", opening overview;
+ * hysenlabs.com, "dao-ailab flash-attention", hardware-boundary section) and fix no format;
+ * this entry point takes OCP FP8 E4M3 codes ("fn": bias 7, 3 mantissa bits, max 448,
+ * NaN = 0x7F / 0xFF, no infinities) with one float32 dequantisation factor per tensor.
+ *   q [B,N,Hq,d], k/v [B,N,Hkv,d] : device pointers to E4M3 codes (one byte each), BSHD
+ *   descale_q/k/v                 : the real inputs are descale_x * decoded code; each
+ *                                   must be finite and > 0
+ *   o [B,N,Hq,d]                  : output, bfloat16; lse [B,Hq,N] float32 natural log
+ *   scale                         : softmax scale applied to the dequantised Q K^T
+ * Computed: the attention of the dequantised inputs, with both products on the 8-bit
+ * matrix cores.  Those sum their 64 code products with less than float32 precision
+ * (measured: error within 2^-11 of the largest single product), so each score is off by up
+ * to about (d/64) 2^-11 |scale| max_c |q_c k_c|, and lse by as much.  The probability
+ * weights are rounded to E4M3 for the second product (each off by at most 2^-4 of itself,
+ * or 2^-10 of the row's largest weight) and O is normalised by the unrounded weight sum.
+ * Returns
+ * FA_ERR_INVALID_ARG also for a factor that is not finite and positive, or
+ * |scale| * descale_q * descale_k above 3e38.  Other rules as fa_fwd.
+ */
+fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                     float descale_q, float descale_k, float descale_v, int B, int Hq, int Hkv,
+                     int N, int d, int causal, int window, float scale, void* stream);
+
+/*
  * Forward, float32 in and out (same contract and layouts as fa_fwd, every tensor float32).
  * Dot products, softmax and accumulation are all float32.
  */

@@ -158,3 +158,24 @@ def test_varlen_workspace():
     assert st == fa.FA_ERR_WORKSPACE
     st = fa.fa_fwd_varlen(None, *([fake] * 4), *args, stream=0)
     assert st == fa.FA_ERR_INVALID_ARG and "null" in fa.fa_last_error()
+
+
+@pytest.mark.parametrize("bad,status", BAD_FWD + [
+    (dict(dq=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(dk=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(dv=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=1e30, dk=1e30), fa.FA_ERR_INVALID_ARG),
+])
+def test_fp8_forward_validation(bad, status):
+    a = dict(B=1, Hq=2, Hkv=2, N=16, d=64, causal=0, window=0, scale=0.125, dq=0.1, dk=0.1,
+             dv=0.1)
+    a.update(bad)
+    fake = 256
+    st = fa.fa_fwd_fp8(fake, fake, fake, fake, fake, a["dq"], a["dk"], a["dv"], a["B"], a["Hq"],
+                       a["Hkv"], a["N"], a["d"], a["causal"], a["window"], a["scale"], stream=0)
+    assert st == status
+    assert fa.fa_last_error().startswith("fa_fwd_fp8")
+    st = fa.fa_fwd_fp8(None, fake, fake, fake, fake, 1.0, 1.0, 1.0, 1, 1, 1, 8, 64, 0, 0, 0.1,
+                       stream=0)
+    assert st == fa.FA_ERR_INVALID_ARG and "null" in fa.fa_last_error()

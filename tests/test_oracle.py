@@ -552,10 +552,11 @@ def test_attn_fwd_fp8_is_attention_of_dequantized_inputs(causal, window):
 
 @pytest.mark.parametrize("offset", [0.0, 1.3, 3.0])
 @pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 7)])
-def test_fp8_error_bound_holds_for_e4m3_rounded_weights(offset, causal, window):
+@pytest.mark.parametrize("delta", [0.0, 0.01])
+def test_fp8_error_bound_holds_for_e4m3_rounded_weights(offset, causal, window, delta):
     """The per-element bound the fp8 GPU tests use, checked against weights rounded to E4M3
     by torch (round to nearest even) at a reference `offset` log2 units below the row max,
-    normalised by the unrounded sum."""
+    normalised by the unrounded sum, with scores perturbed by up to `delta`."""
     torch = pytest.importorskip("torch")
     from tests._parity import fp8_o_bound
     rng = np.random.default_rng(42)
@@ -565,10 +566,12 @@ def test_fp8_error_bound_holds_for_e4m3_rounded_weights(offset, causal, window):
     v = rng.standard_normal((n, d))
     p = attention_probs(q, k, causal, window, 0.3)
     o_ref = p @ v
-    w = p / p.max(axis=1, keepdims=True) * 2.0 ** offset
+    # scores perturbed by up to +-delta (the worst direction pattern of a +-1 draw)
+    pert = np.exp(delta * rng.choice([-1.0, 1.0], size=p.shape))
+    w = p * pert / (p * pert).max(axis=1, keepdims=True) * 2.0 ** offset
     wr = torch.tensor(w).float().to(torch.float8_e4m3fn).double().numpy()
     o_emul = (wr @ v) / w.sum(axis=1, keepdims=True)
-    bound = fp8_o_bound(p, v, o_ref)
+    bound = fp8_o_bound(p, v, o_ref, delta)
     err = np.abs(o_emul - o_ref)
     assert (err <= bound).all(), float((err / bound).max())
     assert (err / bound).max() > 0.02  # the bound is not vacuous for this data
@@ -586,3 +589,13 @@ def test_quantize_e4m3_roundtrip():
     normal = np.abs(xs) >= 2.0 ** -6 * f
     assert (np.abs(y - xs)[normal] <= 2.0 ** -4 * np.abs(xs)[normal] * (1 + 1e-6)).all()
     assert (np.abs(y - xs)[~normal] <= 2.0 ** -10 * f * (1 + 1e-6)).all()
+
+
+def test_fp8_score_error_dominates_brute_force_terms():
+    from tests._parity import fp8_score_error
+    rng = np.random.default_rng(43)
+    q, k = rng.standard_normal((50, 128)) * 3, rng.standard_normal((70, 128))
+    got = fp8_score_error(q, k, -0.2)
+    prod = np.abs(q[:, None, :] * k[None, :, :]).max(axis=2).max(axis=1)
+    smax = np.abs(q @ k.T * 0.2).max(axis=1)
+    assert (got >= 2 * 2.0 ** -10 * 0.2 * prod + 2.0 ** -22 * smax - 1e-15).all()
