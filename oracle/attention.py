@@ -18,6 +18,12 @@ Masking (bmjup.com, section 2.3 and section 3.3):
 * a masked entry has probability 0, i.e. score -inf before the softmax.  It never
   enters the normaliser.
 
+Position bias (bmjup.com, FAQ on inference: the ``alibi_slopes`` argument, no bias when
+it is None; hysenlabs.com, hardware-boundary section: ALiBi): with a slope m_h per query
+head, score_ij = scale * q_i . k_j - m_h * |i - j|, positions counted from the start of the
+sequence, added before the mask and the softmax.  The slopes are constants (no gradient);
+slope 0 is plain attention.
+
 All arithmetic is float64.  Rows are processed in chunks to bound memory; each row's
 softmax always spans its whole allowed key set, so chunking over rows is exact (no
 chunking over keys, no running rescale).
@@ -67,7 +73,7 @@ def _key_span(rows: np.ndarray, n_keys: int, causal: bool, window: int) -> tuple
 
 
 # ------------------------------------------------------------------ row-level core
-def _probs_rows(q, k, rows, causal, window, scale):
+def _probs_rows(q, k, rows, causal, window, scale, slope=0.0):
     """Softmax rows of S = scale * Q K^T for the query ``rows``.
 
     Returns (P, LSE, lo, hi): P covers keys [lo, hi) (zero where masked), LSE is the
@@ -78,6 +84,8 @@ def _probs_rows(q, k, rows, causal, window, scale):
     lo, hi = _key_span(rows, n_keys, causal, window)
     cols = np.arange(lo, hi)
     s = scale * (q[rows] @ k[lo:hi].T)
+    if slope:
+        s = s - slope * np.abs(rows[:, None] - cols[None, :]).astype(np.float64)
     ok = _mask(rows, cols, causal, window)
     s = np.where(ok, s, -np.inf)
     if s.shape[1] == 0:
@@ -104,19 +112,20 @@ def _chunks(n: int, r: int):
 
 
 # ------------------------------------------------------------------ one head
-def attention_probs(q, k, causal=False, window=0, scale=None) -> np.ndarray:
+def attention_probs(q, k, causal=False, window=0, scale=None, slope=0.0) -> np.ndarray:
     """The full N x N probability matrix P of one head (small N only)."""
     q = _as64(q)
     k = _as64(k)
     scale = 1.0 / math.sqrt(q.shape[1]) if scale is None else float(scale)
     rows = np.arange(q.shape[0])
-    p, _, lo, hi = _probs_rows(q, k, rows, causal, window, scale)
+    p, _, lo, hi = _probs_rows(q, k, rows, causal, window, scale, slope)
     full = np.zeros((q.shape[0], k.shape[0]))
     full[:, lo:hi] = p
     return full
 
 
-def attention_probs_rows(q, k, rows, causal=False, window=0, scale=None) -> np.ndarray:
+def attention_probs_rows(q, k, rows, causal=False, window=0, scale=None,
+                         slope=0.0) -> np.ndarray:
     """Rows ``rows`` of the probability matrix P of one head, full width [len(rows), Nk]."""
     q = _as64(q)
     k = _as64(k)
@@ -125,12 +134,12 @@ def attention_probs_rows(q, k, rows, causal=False, window=0, scale=None) -> np.n
     out = np.zeros((rows.size, k.shape[0]))
     for a in range(0, rows.size, 64):
         rr = rows[a:a + 64]
-        p, _, lo, hi = _probs_rows(q, k, rr, causal, window, scale)
+        p, _, lo, hi = _probs_rows(q, k, rr, causal, window, scale, slope)
         out[a:a + 64, lo:hi] = p
     return out
 
 
-def attn_fwd_rows(q, k, v, rows, causal=False, window=0, scale=None):
+def attn_fwd_rows(q, k, v, rows, causal=False, window=0, scale=None, slope=0.0):
     """O and LSE of one head for the selected query ``rows`` only.
 
     q: [Nq, d], k: [Nk, d], v: [Nk, dv] of one (batch, query head) pair.
@@ -144,13 +153,14 @@ def attn_fwd_rows(q, k, v, rows, causal=False, window=0, scale=None):
     lse = np.zeros(rows.size)
     for a in range(0, rows.size, 64):
         rr = rows[a:a + 64]
-        p, l, lo, hi = _probs_rows(q, k, rr, causal, window, scale)
+        p, l, lo, hi = _probs_rows(q, k, rr, causal, window, scale, slope)
         o[a:a + 64] = p @ v[lo:hi]
         lse[a:a + 64] = l
     return o, lse
 
 
-def attn_fwd_head(q, k, v, causal=False, window=0, scale=None, row_chunk=DEFAULT_ROW_CHUNK):
+def attn_fwd_head(q, k, v, causal=False, window=0, scale=None, row_chunk=DEFAULT_ROW_CHUNK,
+                  slope=0.0):
     """Forward of one head: O = softmax(scale * Q K^T (masked)) V and its LSE.
 
     (ainews.cool "flash-attention transformer optimization", technical deep dive:
@@ -162,13 +172,13 @@ def attn_fwd_head(q, k, v, causal=False, window=0, scale=None, row_chunk=DEFAULT
     o = np.zeros((n, v.shape[1]))
     lse = np.zeros(n)
     for rows in _chunks(n, row_chunk):
-        p, l, lo, hi = _probs_rows(q, k, rows, causal, window, scale)
+        p, l, lo, hi = _probs_rows(q, k, rows, causal, window, scale, slope)
         o[rows] = p @ v[lo:hi]
         lse[rows] = l
     return o, lse
 
 
-def _bwd_rows(q, k, v, do, rows, causal, window, scale):
+def _bwd_rows(q, k, v, do, rows, causal, window, scale, slope=0.0):
     """Backward quantities for ``rows`` of one head.
 
     With L = sum(O * dO) (the upstream gradient dO), the chain rule through the
@@ -180,14 +190,15 @@ def _bwd_rows(q, k, v, do, rows, causal, window, scale):
         dK_j += scale * dS_ij q_i ,  dV_j += P_ij dO_i
     Returns (P, dS, D, lo, hi) for the caller to contract.
     """
-    p, _, lo, hi = _probs_rows(q, k, rows, causal, window, scale)
+    p, _, lo, hi = _probs_rows(q, k, rows, causal, window, scale, slope)
     dp = do[rows] @ v[lo:hi].T
     dvec = (p * dp).sum(axis=1)
     ds = p * (dp - dvec[:, None])
     return p, ds, dvec, lo, hi
 
 
-def attn_bwd_head(q, k, v, do, causal=False, window=0, scale=None, row_chunk=DEFAULT_ROW_CHUNK):
+def attn_bwd_head(q, k, v, do, causal=False, window=0, scale=None, row_chunk=DEFAULT_ROW_CHUNK,
+                  slope=0.0):
     """Gradients of L = sum(O * dO) for one head: (dQ, dK, dV, D).
 
     The pages state only that the backward rebuilds the attention matrix from Q, K
@@ -202,7 +213,7 @@ def attn_bwd_head(q, k, v, do, causal=False, window=0, scale=None, row_chunk=DEF
     dv = np.zeros_like(v)
     dvec = np.zeros(n)
     for rows in _chunks(n, row_chunk):
-        p, ds, d_r, lo, hi = _bwd_rows(q, k, v, do, rows, causal, window, scale)
+        p, ds, d_r, lo, hi = _bwd_rows(q, k, v, do, rows, causal, window, scale, slope)
         dq[rows] = scale * (ds @ k[lo:hi])
         dk[lo:hi] += scale * (ds.T @ q[rows])
         dv[lo:hi] += p.T @ do[rows]
@@ -210,7 +221,7 @@ def attn_bwd_head(q, k, v, do, causal=False, window=0, scale=None, row_chunk=DEF
     return dq, dk, dv, dvec
 
 
-def attn_bwd_dq_rows(q, k, v, do, rows, causal=False, window=0, scale=None):
+def attn_bwd_dq_rows(q, k, v, do, rows, causal=False, window=0, scale=None, slope=0.0):
     """dQ (and D) of one head for the selected query ``rows`` only (row-local)."""
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
     scale = 1.0 / math.sqrt(q.shape[1]) if scale is None else float(scale)
@@ -219,14 +230,14 @@ def attn_bwd_dq_rows(q, k, v, do, rows, causal=False, window=0, scale=None):
     dvec = np.zeros(rows.size)
     for a in range(0, rows.size, 64):
         rr = rows[a:a + 64]
-        _, ds, d_r, lo, hi = _bwd_rows(q, k, v, do, rr, causal, window, scale)
+        _, ds, d_r, lo, hi = _bwd_rows(q, k, v, do, rr, causal, window, scale, slope)
         dq[a:a + 64] = scale * (ds @ k[lo:hi])
         dvec[a:a + 64] = d_r
     return dq, dvec
 
 
 def attn_bwd_dkdv_cols(q, k, v, do, cols, causal=False, window=0, scale=None,
-                       row_chunk=DEFAULT_ROW_CHUNK):
+                       row_chunk=DEFAULT_ROW_CHUNK, slope=0.0):
     """This query head's contribution to dK and dV at the selected key ``cols``.
 
     Only query rows that can attend some selected key are visited (causal: rows
@@ -244,7 +255,7 @@ def attn_bwd_dkdv_cols(q, k, v, do, cols, causal=False, window=0, scale=None,
     dv = np.zeros((cols.size, v.shape[1]))
     for a in range(r0, r1, row_chunk):
         rows = np.arange(a, min(r1, a + row_chunk))
-        p, ds, _, lo, hi = _bwd_rows(q, k, v, do, rows, causal, window, scale)
+        p, ds, _, lo, hi = _bwd_rows(q, k, v, do, rows, causal, window, scale, slope)
         sel = cols - lo
         inside = (sel >= 0) & (sel < hi - lo)
         if not inside.any():
@@ -269,13 +280,22 @@ def _check_shapes(q, k, v):
 
 
 def _fwd_task(args):
-    q, k, v, causal, window, scale, row_chunk = args
-    return attn_fwd_head(q, k, v, causal, window, scale, row_chunk)
+    q, k, v, causal, window, scale, row_chunk, *slope = args
+    return attn_fwd_head(q, k, v, causal, window, scale, row_chunk, *slope)
 
 
 def _bwd_task(args):
-    q, k, v, do, causal, window, scale, row_chunk = args
-    return attn_bwd_head(q, k, v, do, causal, window, scale, row_chunk)
+    q, k, v, do, causal, window, scale, row_chunk, *slope = args
+    return attn_bwd_head(q, k, v, do, causal, window, scale, row_chunk, *slope)
+
+
+def _slopes(alibi_slopes, hq: int) -> np.ndarray:
+    if alibi_slopes is None:
+        return np.zeros(hq)
+    m = np.asarray(alibi_slopes, dtype=np.float64).reshape(-1)
+    if m.size != hq:
+        raise ValueError(f"alibi_slopes must hold one slope per query head ({hq})")
+    return m
 
 
 def _limit_blas_threads():
@@ -303,7 +323,7 @@ def default_workers(_=None) -> int:
 
 
 def attn_fwd(q, k, v, causal=False, window=0, scale=None, row_chunk=DEFAULT_ROW_CHUNK,
-             workers=None):
+             workers=None, alibi_slopes=None):
     """Forward over [B, N, Hq, d] inputs (KV: [B, N, Hkv, d]).
 
     Returns O [B, N, Hq, dv] and LSE [B, Hq, N], float64.  ``workers`` > 1 runs the
@@ -313,8 +333,9 @@ def attn_fwd(q, k, v, causal=False, window=0, scale=None, row_chunk=DEFAULT_ROW_
     b, n, hq, hkv, d = _check_shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     g = hq // hkv
-    tasks = [(q[bi, :, h], k[bi, :, h // g], v[bi, :, h // g], causal, window, scale, row_chunk)
-             for bi in range(b) for h in range(hq)]
+    m = _slopes(alibi_slopes, hq)
+    tasks = [(q[bi, :, h], k[bi, :, h // g], v[bi, :, h // g], causal, window, scale, row_chunk,
+              m[h]) for bi in range(b) for h in range(hq)]
     res = _run(tasks, _fwd_task, workers)
     o = np.zeros((b, n, hq, v.shape[3]))
     lse = np.zeros((b, hq, n))
@@ -326,7 +347,7 @@ def attn_fwd(q, k, v, causal=False, window=0, scale=None, row_chunk=DEFAULT_ROW_
 
 
 def attn_bwd(q, k, v, do, causal=False, window=0, scale=None, row_chunk=DEFAULT_ROW_CHUNK,
-             workers=None):
+             workers=None, alibi_slopes=None):
     """Backward over full tensors: (dQ [B,N,Hq,d], dK, dV [B,N,Hkv,d], D [B,Hq,N]).
 
     dK and dV of a KV head are the sums over the query heads of its group (the
@@ -336,8 +357,9 @@ def attn_bwd(q, k, v, do, causal=False, window=0, scale=None, row_chunk=DEFAULT_
     b, n, hq, hkv, d = _check_shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     g = hq // hkv
+    m = _slopes(alibi_slopes, hq)
     tasks = [(q[bi, :, h], k[bi, :, h // g], v[bi, :, h // g], do[bi, :, h], causal, window,
-              scale, row_chunk) for bi in range(b) for h in range(hq)]
+              scale, row_chunk, m[h]) for bi in range(b) for h in range(hq)]
     res = _run(tasks, _bwd_task, workers)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
@@ -370,7 +392,7 @@ def _check_cu(cu_seqlens, total: int) -> np.ndarray:
 
 
 def attn_fwd_varlen(q, k, v, cu_seqlens, causal=False, window=0, scale=None,
-                    row_chunk=DEFAULT_ROW_CHUNK):
+                    row_chunk=DEFAULT_ROW_CHUNK, alibi_slopes=None):
     """Forward over packed sequences: q [T, Hq, d], k, v [T, Hkv, d].
 
     Sequence s is rows cu_seqlens[s] .. cu_seqlens[s+1]-1 of every tensor.  It is the
@@ -385,6 +407,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, causal=False, window=0, scale=None,
     cu = _check_cu(cu_seqlens, t)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     g = hq // hkv
+    m = _slopes(alibi_slopes, hq)
     o = np.zeros((t, hq, v.shape[2]))
     lse = np.zeros((hq, t))
     for s0, s1 in zip(cu[:-1], cu[1:]):
@@ -392,14 +415,14 @@ def attn_fwd_varlen(q, k, v, cu_seqlens, causal=False, window=0, scale=None,
             continue
         for h in range(hq):
             oh, lh = attn_fwd_head(q[s0:s1, h], k[s0:s1, h // g], v[s0:s1, h // g], causal,
-                                   window, scale, row_chunk)
+                                   window, scale, row_chunk, m[h])
             o[s0:s1, h] = oh
             lse[h, s0:s1] = lh
     return o, lse
 
 
 def attn_bwd_varlen(q, k, v, do, cu_seqlens, causal=False, window=0, scale=None,
-                    row_chunk=DEFAULT_ROW_CHUNK):
+                    row_chunk=DEFAULT_ROW_CHUNK, alibi_slopes=None):
     """Backward over packed sequences: (dQ [T,Hq,d], dK, dV [T,Hkv,d], D [Hq,T]), each
     sequence on its own as in attn_fwd_varlen; dK, dV of a KV head summed over its group."""
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
@@ -408,6 +431,7 @@ def attn_bwd_varlen(q, k, v, do, cu_seqlens, causal=False, window=0, scale=None,
     cu = _check_cu(cu_seqlens, t)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     g = hq // hkv
+    m = _slopes(alibi_slopes, hq)
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -417,7 +441,8 @@ def attn_bwd_varlen(q, k, v, do, cu_seqlens, causal=False, window=0, scale=None,
             continue
         for h in range(hq):
             dqh, dkh, dvh, dh = attn_bwd_head(q[s0:s1, h], k[s0:s1, h // g], v[s0:s1, h // g],
-                                              do[s0:s1, h], causal, window, scale, row_chunk)
+                                              do[s0:s1, h], causal, window, scale, row_chunk,
+                                              m[h])
             dq[s0:s1, h] = dqh
             dk[s0:s1, h // g] += dkh
             dv[s0:s1, h // g] += dvh

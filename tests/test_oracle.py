@@ -599,3 +599,93 @@ def test_fp8_score_error_dominates_brute_force_terms():
     prod = np.abs(q[:, None, :] * k[None, :, :]).max(axis=2).max(axis=1)
     smax = np.abs(q @ k.T * 0.2).max(axis=1)
     assert (got >= 2 * 2.0 ** -10 * 0.2 * prod + 2.0 ** -22 * smax - 1e-15).all()
+
+
+# ------------------------------------------------------------------ ALiBi position bias
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 6), (False, 5)])
+def test_alibi_matches_torch_float_bias_and_autograd(causal, window):
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(50)
+    b, n, hq, hkv, d = 2, 23, 4, 2, 8
+    q, k, v, do = (rng.standard_normal((b, n, h, d)) for h in (hq, hkv, hkv, hq))
+    slopes = np.array([0.5, 0.125, -0.05, 0.0])
+    o, lse = attn_fwd(q, k, v, causal, window, 0.3, alibi_slopes=slopes)
+    dq, dk, dv, _ = attn_bwd(q, k, v, do, causal, window, 0.3, alibi_slopes=slopes)
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    ok = torch.ones(n, n, dtype=torch.bool)
+    if causal:
+        ok &= j <= i
+    if window:
+        ok &= j >= i - window + 1
+    bias = -torch.tensor(slopes)[:, None, None] * (i - j).abs().double()  # [hq, n, n]
+    bias = bias.masked_fill(~ok, float("-inf"))[None]
+    g = hq // hkv
+    tq = torch.tensor(q).transpose(1, 2).requires_grad_()
+    tk = torch.tensor(k).transpose(1, 2).requires_grad_()
+    tv = torch.tensor(v).transpose(1, 2).requires_grad_()
+    out = F.scaled_dot_product_attention(tq, tk.repeat_interleave(g, dim=1),
+                                         tv.repeat_interleave(g, dim=1), attn_mask=bias, scale=0.3)
+    out.backward(torch.tensor(do).transpose(1, 2))
+    np.testing.assert_allclose(o, out.detach().transpose(1, 2).numpy(), atol=1e-12)
+    s = tq.detach() @ tk.detach().repeat_interleave(g, dim=1).transpose(-1, -2) * 0.3 + bias
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.transpose(1, 2).numpy(), atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.transpose(1, 2).numpy(), atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.transpose(1, 2).numpy(), atol=1e-11)
+
+
+def test_alibi_zero_queries_closed_form():
+    """Q = 0 leaves only the bias: causal row i weighs key i - t by e^(-m t), so
+    LSE_i = ln((1 - e^(-m (i+1))) / (1 - e^(-m))) and O_i is that geometric average of V."""
+    rng = np.random.default_rng(51)
+    n, d, m = 40, 4, 0.3
+    q = np.zeros((1, n, 1, d))
+    k = rng.standard_normal((1, n, 1, d))
+    v = rng.standard_normal((1, n, 1, d))
+    o, lse = attn_fwd(q, k, v, True, 0, 0.7, alibi_slopes=[m])
+    i = np.arange(n)
+    np.testing.assert_allclose(lse[0, 0], np.log((1 - np.exp(-m * (i + 1))) / (1 - np.exp(-m))),
+                               rtol=1e-13)
+    for r in (0, 1, 17, n - 1):
+        w = np.exp(-m * (r - np.arange(r + 1)))
+        np.testing.assert_allclose(o[0, r, 0], w @ v[0, :r + 1, 0] / w.sum(), rtol=1e-12)
+
+
+def test_alibi_gradients_match_finite_differences():
+    rng = np.random.default_rng(52)
+    b, n, h, d = 1, 7, 2, 3
+    q, k, v, do = (rng.standard_normal((b, n, h, d)) for _ in range(4))
+    slopes = [0.4, 0.9]
+    dq, dk, dv, _ = attn_bwd(q, k, v, do, True, 4, 0.5, alibi_slopes=slopes)
+
+    def loss(qq, kk, vv):
+        return float((attn_fwd(qq, kk, vv, True, 4, 0.5, alibi_slopes=slopes)[0] * do).sum())
+
+    eps = 1e-6
+    for x, g in ((q, dq), (k, dk), (v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args_p = [xp if y is x else y for y in (q, k, v)]
+            args_m = [xm if y is x else y for y in (q, k, v)]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8)
+
+
+def test_alibi_packed_positions_start_at_each_sequence():
+    rng = np.random.default_rng(53)
+    n, nb, hq, d = 11, 3, 2, 4
+    cu, q, k, v, do = _packed(rng, [n] * nb, hq, hq, d)
+    sl = [0.3, 0.05]
+    o, lse = attn_fwd_varlen(q, k, v, cu, True, 0, 0.5, alibi_slopes=sl)
+    ob, lseb = attn_fwd(q.reshape(nb, n, hq, d), k.reshape(nb, n, hq, d), v.reshape(nb, n, hq, d),
+                        True, 0, 0.5, alibi_slopes=sl)
+    np.testing.assert_array_equal(o, ob.reshape(nb * n, hq, d))
+    g = attn_bwd_varlen(q, k, v, do, cu, True, 0, 0.5, alibi_slopes=sl)
+    gb = attn_bwd(q.reshape(nb, n, hq, d), k.reshape(nb, n, hq, d), v.reshape(nb, n, hq, d),
+                  do.reshape(nb, n, hq, d), True, 0, 0.5, alibi_slopes=sl)
+    for a, bt in zip(g[:3], gb[:3]):
+        np.testing.assert_array_equal(a, bt.reshape(a.shape))
