@@ -116,13 +116,17 @@ def _head_tasks(w, q, k, v, do, packed):
                 None if do is None else f64(do[a:a + n, h]), w.causal, w.window, w.scale,
                 oa.DEFAULT_ROW_CHUNK)
     else:
+        from exact_io_aware_fa2_amd.workloads import alibi_slopes
         flop = 4.0 * attended_pairs(w.N, w.causal, w.window) * w.d
+        # ALiBi: the slope each head's oracle task adds (the float32 value the kernels read)
+        slopes = ([float(np.float32(m)) for m in alibi_slopes(w.Hq)]
+                  if getattr(w, "alibi", False) else None)
         for i in range(w.B * w.Hq):
             b, h = i // w.Hq, i % w.Hq
             yield flop, lambda b=b, h=h: (
                 f64(q[b, :, h]), f64(k[b, :, h // g]), f64(v[b, :, h // g]),
                 None if do is None else f64(do[b, :, h]), w.causal, w.window, w.scale,
-                oa.DEFAULT_ROW_CHUNK)
+                oa.DEFAULT_ROW_CHUNK) + ((slopes[h],) if slopes else ())
 
 
 def cpu_baseline(w, q, k, v, do, packed=False, max_workers: int = 16):
@@ -192,14 +196,16 @@ def main() -> int:
 
     import torch
     from exact_io_aware_fa2_amd import fa
-    from exact_io_aware_fa2_amd.workloads import (FP8_WORKLOADS, HEADLINE, VARLEN_WORKLOADS,
-                                                  WORKLOADS, make_fp8_inputs, make_inputs,
+    from exact_io_aware_fa2_amd.workloads import (ALIBI_WORKLOADS, FP8_WORKLOADS, HEADLINE,
+                                                  VARLEN_WORKLOADS, WORKLOADS, alibi_slopes,
+                                                  make_fp8_inputs, make_inputs,
                                                   make_varlen_inputs)
 
     name = args.workload or HEADLINE
     packed = name in VARLEN_WORKLOADS
     fp8 = name in FP8_WORKLOADS
-    w = VARLEN_WORKLOADS[name] if packed else FP8_WORKLOADS[name] if fp8 else WORKLOADS[name]
+    w = (VARLEN_WORKLOADS[name] if packed else FP8_WORKLOADS[name] if fp8 else
+         ALIBI_WORKLOADS[name] if name in ALIBI_WORKLOADS else WORKLOADS[name])
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -227,6 +233,10 @@ def main() -> int:
         F = fwd_flops(w)
         config = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                   "causal": w.causal, "window": w.window, "scale": w.scale}
+    slopes = None
+    if getattr(w, "alibi", False):
+        slopes = torch.tensor(alibi_slopes(w.Hq), dtype=torch.float32, device=dev)
+        config["alibi_slopes"] = "2^(-8 h / Hq), h = 1 .. Hq"
     o = torch.empty(q.shape, device=dev, dtype=torch.bfloat16) if fp8 else torch.empty_like(q)
     bwd = do is not None and w.dtype == "bf16"
     if bwd:
@@ -245,6 +255,9 @@ def main() -> int:
         elif fp8:
             st = fa.fa_fwd_fp8(q, k, v, o, lse, *factors, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal,
                                w.window, w.scale, sh)
+        elif slopes is not None:
+            st = fa.fa_fwd(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
+                           w.scale, sh, alibi_slopes=slopes)
         else:
             st = fwd_fn(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
                         w.scale, sh)
@@ -257,7 +270,7 @@ def main() -> int:
                                   w.d, w.causal, w.window, w.scale, ws, ws_bytes, sh)
         else:
             st = fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.B, w.Hq, w.Hkv, w.N, w.d,
-                           w.causal, w.window, w.scale, ws, ws_bytes, sh)
+                           w.causal, w.window, w.scale, ws, ws_bytes, sh, alibi_slopes=slopes)
         if st != fa.FA_OK:
             raise RuntimeError(fa.fa_last_error())
 

@@ -88,7 +88,7 @@ extern "C" {
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int Hq, int Hkv, int N, int d, int causal, int window, float scale,
-                 void* stream) {
+                 const float* alibi_slopes, void* stream) {
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "fa_fwd: null pointer");
   fa_status st = check_common("fa_fwd", B, Hq, Hkv, N, d, causal, window, scale);
   if (st != FA_OK) return st;
@@ -99,6 +99,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;
   fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal ? 1 : 0, window, c2,
                 scale * fa::kHostLog2e, scale < 0.f ? 1 : 0};
+  a.slopes = alibi_slopes;
   return launched("fa_fwd", fa::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
@@ -146,7 +147,7 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, i
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
                  int N, int d, int causal, int window, float scale, void* workspace,
-                 size_t workspace_bytes, void* stream) {
+                 size_t workspace_bytes, const float* alibi_slopes, void* stream) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
     return fail(FA_ERR_INVALID_ARG, "fa_bwd: null pointer");
   fa_status st = check_common("fa_bwd", B, Hq, Hkv, N, d, causal, window, scale);
@@ -162,6 +163,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                 causal ? 1 : 0, window, scale, scale * fa::kHostLog2e, g_time_start,
                 g_time_stop};
   g_time_start = g_time_stop = nullptr;
+  a.slopes = alibi_slopes;
   return launched("fa_bwd", fa::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 
@@ -174,7 +176,8 @@ fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
 
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
-                        int Hkv, int d, int causal, int window, float scale, void* stream) {
+                        int Hkv, int d, int causal, int window, float scale,
+                        const float* alibi_slopes, void* stream) {
   if (!q || !k || !v || !o || !lse)
     return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: null pointer");
   fa_status st = check_varlen("fa_fwd_varlen", cu_seqlens, num_seqs, total, max_seqlen, Hq,
@@ -183,6 +186,7 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
   const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;  // as in fa_fwd
   fa::FwdArgs a{q, k, v, o, lse, num_seqs, Hq, Hkv, max_seqlen, d, causal ? 1 : 0, window,
                 c2, scale * fa::kHostLog2e, scale < 0.f ? 1 : 0, cu_seqlens, total};
+  a.slopes = alibi_slopes;
   return launched("fa_fwd_varlen", fa::launch_fwd_bf16(a, (hipStream_t)stream));
 }
 
@@ -197,7 +201,7 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         const void* dO, const float* lse, void* dq, void* dk, void* dv,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
                         int Hkv, int d, int causal, int window, float scale, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, const float* alibi_slopes, void* stream) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
     return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: null pointer");
   fa_status st = check_varlen("fa_bwd_varlen", cu_seqlens, num_seqs, total, max_seqlen, Hq,
@@ -213,6 +217,7 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                 Hkv, max_seqlen, d, causal ? 1 : 0, window, scale, scale * fa::kHostLog2e,
                 g_time_start, g_time_stop, cu_seqlens, total};
   g_time_start = g_time_stop = nullptr;
+  a.slopes = alibi_slopes;
   return launched("fa_bwd_varlen", fa::launch_bwd_bf16(a, (hipStream_t)stream));
 }
 

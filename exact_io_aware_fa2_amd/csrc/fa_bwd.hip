@@ -103,12 +103,13 @@ struct KVCfg {
   static constexpr int LDS_BYTES = 2 * (BUF * 2 + 2 * BQ * 4);  // + LSE, D; double buffered
 };
 
-template <int D>
+template <int D, int AL>
 __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int B, int Hq, int Hkv, int Nmax,
-    int causal, int window, float c, float scale, const int* __restrict__ cu, int ntot) {
+    int causal, int window, float c, float scale, const int* __restrict__ cu, int ntot,
+    const float* __restrict__ slopes) {
   using Cfg = KVCfg<D>;
   constexpr int BKN = Cfg::BKN, BQ = Cfg::BQ, MT = Cfg::MT, DH = Cfg::DH;
   constexpr int NSPLIT = Cfg::NSPLIT, STR = Cfg::STR, TSTR = Cfg::TSTR;
@@ -152,6 +153,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int qb_hi = (row_end + BQ - 1) / BQ;
   const int nq = max(0, qb_hi - qb_lo);
   const int total_it = G * nq;
+  // ALiBi slope (log2 units) of the query head of step it
+  auto slope_of = [&](int it) { return AL != 0 ? slopes[hkv * G + it / nq] * kLog2e : 0.f; };
 
   f32x16 dk[NDH], dv[NDH];
 #pragma unroll
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       dreg = n < N ? Dv[li] : 0.f;
     }
   };
-  auto swrite = [&](int buf) {
+  auto swrite = [&](int buf, int buf_it) {
     bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + buf * BUFB);
     bf16_t* sO = sQ + Cfg::SQ;
     bf16_t* sQT = sO + Cfg::SQ;
@@ -216,14 +219,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       }
     }
     if (tid < BQ) {
-      sL[tid] = lreg;
+      // causal position bias: LSE + slope2 (row - r0) is staged, slope2 (key - r0) added per
+      // lane (both small near the diagonal, where the weights are not negligible)
+      sL[tid] = AL == 1 ? lreg + slope_of(buf_it) * tid : lreg;
       sL[BQ + tid] = dreg;
     }
   };
 
   if (total_it > 0) {
     gload(0);
-    swrite(0);
+    swrite(0, 0);
     if (total_it > 1) gload(1);
   }
   __syncthreads();
@@ -261,15 +266,23 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           dp[mt] = mfma32(oa_op[cc], vop[cc], dp[mt]);
         }
       }
-      // P = exp2(S c - LSE log2 e), masked entries 0 (selects under a wave-uniform branch).
+      // P = exp2(S c + bias - LSE log2 e), masked entries 0 (selects under a wave-uniform
+      // branch).  The position bias: see alibi_addend (here the lane is the key).
+      const float sl2 = slope_of(it);
+      const float kstep = sl2 * (float)(key - r0);
+      const float rbase = (float)(r0 + 4 * hh - key);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + 32 * mt + 8 * g4 + 4 * hh);
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            s[mt][4 * g4 + e] = fast_exp2(fmaf(s[mt][4 * g4 + e], c, -L4[e]));
+          for (int e = 0; e < 4; ++e) {
+            const float xr = AL == 1 ? kstep - L4[e]
+                                     : alibi_addend<AL>(sl2, rbase, (float)(32 * mt + 8 * g4 + e),
+                                                        L4[e]);
+            s[mt][4 * g4 + e] = fast_exp2(fmaf(s[mt][4 * g4 + e], c, xr));
+          }
         }
       }
       const bool need_mask = (kw0 + 32 > N) || (causal && kw0 + 31 > r0) ||
@@ -330,7 +343,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       }
     }
     if (it + 1 < total_it) {
-      swrite(buf ^ 1);
+      swrite(buf ^ 1, it + 1);
       if (it + 2 < total_it) gload(it + 2);
     }
     __syncthreads();
@@ -377,12 +390,13 @@ struct KV8Cfg {
   static constexpr int LDS_BYTES = SV * 2 + 2 * BUFB;  // V block + double-buffered staging
 };
 
-template <int D>
+template <int D, int AL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     bf16_t* __restrict__ dK, bf16_t* __restrict__ dV, int B, int Hq, int Hkv, int Nmax,
-    int causal, int window, float c, float scale, const int* __restrict__ cu, int ntot) {
+    int causal, int window, float c, float scale, const int* __restrict__ cu, int ntot,
+    const float* __restrict__ slopes) {
   using Cfg = KV8Cfg<D>;
   constexpr int NT = Cfg::NT, BKN = Cfg::BKN, BQ = Cfg::BQ, STR = Cfg::STR, TSTR = Cfg::TSTR;
   constexpr int NC = D / 16, ND = D / 32;
@@ -425,6 +439,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   const int qb_hi = (row_end + BQ - 1) / BQ;
   const int nq = max(0, qb_hi - qb_lo);
   const int total_it = G * nq;
+  // ALiBi slope (log2 units) of the query head of step it
+  auto slope_of = [&](int it) { return AL != 0 ? slopes[hkv * G + it / nq] * kLog2e : 0.f; };
 
   f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -491,7 +507,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     }
     if (tid < BQ) {
       const bool in = step_r0(it) + tid < N;
-      sL[tid] = in ? lraw * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
+      // +inf -> P = 0 on padding rows.  Causal position bias: LSE + slope2 (row - r0) is
+      // staged and slope2 (key - r0) added per lane, both small near the diagonal.
+      sL[tid] = in ? lraw * kLog2e + (AL == 1 ? slope_of(it) * tid : 0.f) : INFINITY;
       sL[BQ + tid] = in ? draw : 0.f;
     }
   };
@@ -531,13 +549,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
         if (cc % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
-      // P = exp2(S c - LSE log2 e), masked entries 0; dS = P (dP - D).
+      // P = exp2(S c + bias - LSE log2 e), masked entries 0; dS = P (dP - D).  The position
+      // bias: see alibi_addend (here the lane is the key).
       float pv[16];
+      const float sl2 = slope_of(it);
+      const float kstep = sl2 * (float)(key - r0);
+      const float rbase = (float)(r0 + 4 * hh - key);
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + 8 * g4 + 4 * hh);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pv[4 * g4 + e] = fast_exp2(fmaf(s[4 * g4 + e], c, -L4[e]));
+        for (int e = 0; e < 4; ++e) {
+          const float xr = AL == 1 ? kstep - L4[e]
+                                   : alibi_addend<AL>(sl2, rbase, (float)(8 * g4 + e), L4[e]);
+          pv[4 * g4 + e] = fast_exp2(fmaf(s[4 * g4 + e], c, xr));
+        }
       }
       const bool need_mask = (kw0 + 32 > N) || (causal && kw0 + 31 > r0) ||
                              (window > 0 && kw0 < r0 + BQ - window);
@@ -628,12 +654,12 @@ struct QCfg {
   static constexpr int LDS_BYTES = 2 * BUF * 2;  // double buffered
 };
 
-template <int D>
+template <int D, int AL>
 __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     const bf16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     bf16_t* __restrict__ dQ, int B, int Hq, int Hkv, int Nmax, int causal, int window, float c,
-    float scale, const int* __restrict__ cu, int ntot) {
+    float scale, const int* __restrict__ cu, int ntot, const float* __restrict__ slopes) {
   using Cfg = QCfg<D>;
   constexpr int NT = Cfg::NT, BM = Cfg::BM, BN = Cfg::BN, KSTR = Cfg::KSTR, TSTR = Cfg::TSTR;
   constexpr int NC = D / 16, ND = D / 32;
@@ -672,6 +698,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   const size_t li = stat_base(cu, ntot, b, Hq, hq, Nmax, seq0) + row;
   const float lse2 = row < N ? LSE[li] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
   const float dval = row < N ? Dv[li] : 0.f;
+  const float slope2 = AL != 0 ? slopes[hq] * kLog2e : 0.f;
 
   int kv_lo = 0, kv_hi = N;
   if (causal) kv_hi = min(N, m0 + BM);
@@ -825,8 +852,13 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
         }
         // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D); masked entries 0.
         float p[16];
+        {  // position bias: see alibi_addend (key - row of element 0 is k0 + 4 hh - row)
+          const float dbase = AL != 0 ? (float)(k0 + 4 * hh - row) : 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = fast_exp2(fmaf(s[r], c, -lse2));
+          for (int r = 0; r < 16; ++r)
+            p[r] = fast_exp2(fmaf(s[r], c, alibi_addend<AL>(slope2, dbase,
+                                                            (float)(8 * (r >> 2) + (r & 3)), lse2)));
+        }
         const bool need_mask = (k0 + 32 > N) || (causal && k0 + 31 > wr0) ||
                                (window > 0 && k0 < wr0 + 32 - window);
         if (need_mask) {
@@ -881,7 +913,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
 }
 
 // =====================================================================================
-template <int D>
+template <int D, int AL>
 static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   using KC = KVCfg<D>;
   using K8 = KV8Cfg<D <= 128 ? D : 128>;
@@ -889,14 +921,14 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   constexpr bool kWide = D <= 128;  // 8-wave key-block kernel
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t e = kWide ? hipFuncSetAttribute((const void*)bwd_dkdv8_kernel<D <= 128 ? D : 128>,
+    hipError_t e = kWide ? hipFuncSetAttribute((const void*)bwd_dkdv8_kernel<D <= 128 ? D : 128, AL>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                K8::LDS_BYTES)
-                         : hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D>,
+                         : hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, AL>,
                                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                                KC::LDS_BYTES);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D>,
+    e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D, AL>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, QC::LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_done = true;
@@ -915,18 +947,18 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   if constexpr (kWide) {
     constexpr int DW = D <= 128 ? D : 128;
     const int num_kb = (a.N + K8::BKN - 1) / K8::BKN;
-    hipLaunchKernelGGL(bwd_dkdv8_kernel<DW>, dim3(a.B * a.Hkv * num_kb), dim3(K8::NT),
+    hipLaunchKernelGGL((bwd_dkdv8_kernel<DW, AL>), dim3(a.B * a.Hkv * num_kb), dim3(K8::NT),
                        K8::LDS_BYTES, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
                        (const bf16_t*)a.v, (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dk,
                        (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window,
-                       a.c_log2_signed, a.scale, a.cu, a.ntot);
+                       a.c_log2_signed, a.scale, a.cu, a.ntot, a.slopes);
   } else {
     const int num_kb = (a.N + KC::BKN - 1) / KC::BKN;
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(a.B * a.Hkv * num_kb * KC::NSPLIT),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, AL>), dim3(a.B * a.Hkv * num_kb * KC::NSPLIT),
                        dim3(KC::NT), KC::LDS_BYTES, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
                        (const bf16_t*)a.v, (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dk,
                        (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window,
-                       a.c_log2_signed, a.scale, a.cu, a.ntot);
+                       a.c_log2_signed, a.scale, a.cu, a.ntot, a.slopes);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -935,18 +967,24 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const int num_m = (a.N + QC::BM - 1) / QC::BM;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(a.B * a.Hq * num_m), dim3(QC::NT), QC::LDS_BYTES, st,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, AL>), dim3(a.B * a.Hq * num_m), dim3(QC::NT), QC::LDS_BYTES, st,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v,
                      (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dq, a.B, a.Hq, a.Hkv, a.N,
-                     a.causal, a.window, a.c_log2_signed, a.scale, a.cu, a.ntot);
+                     a.causal, a.window, a.c_log2_signed, a.scale, a.cu, a.ntot, a.slopes);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_al(const BwdArgs& a, hipStream_t st) {
+  if (a.slopes == nullptr) return launch_bwd_d<D, 0>(a, st);
+  return a.causal ? launch_bwd_d<D, 1>(a, st) : launch_bwd_d<D, 2>(a, st);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st) {
   switch (a.d) {
-    case 64: return launch_bwd_d<64>(a, st);
-    case 128: return launch_bwd_d<128>(a, st);
-    case 256: return launch_bwd_d<256>(a, st);
+    case 64: return launch_bwd_al<64>(a, st);
+    case 128: return launch_bwd_al<128>(a, st);
+    case 256: return launch_bwd_al<256>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -216,6 +216,25 @@ __device__ __forceinline__ void store_4x8_transposed(bf16_t* lds, int ts, int lr
   }
 }
 
+// ALiBi position bias, in log2 units: the score of (row, key) gets -slope log2(e) |row - key|
+// (bmjup.com, FAQ on inference: the alibi_slopes argument; hysenlabs.com, hardware-boundary
+// section).  AL = 0: no bias.  AL = 1 (causal: every allowed key is at or before the row):
+// the bias is linear in the key, slope2 (key - row), one FMA per score with the in-tile key
+// offset as a literal.  AL = 2 (no causal mask): slope2 |key - row| needs the distance, one
+// add and one FMA with an absolute-value operand.  `dbase` is key - row of the lane's
+// element 0, `off` the element's key offset from it; the result is the exp2 addend
+// bias - mref.  slope2 = slope * log2(e), any finite value.
+template <int AL>
+__device__ __forceinline__ float alibi_addend(float slope2, float dbase, float off, float mref) {
+  if constexpr (AL == 0) {
+    return -mref;
+  } else if constexpr (AL == 1) {
+    return fmaf(slope2, off, fmaf(slope2, dbase, -mref));
+  } else {
+    return fmaf(-slope2, fabsf(dbase + off), -mref);
+  }
+}
+
 // Work order over (batch entry, head, block) triples; `rank` 0 is the heaviest block of a
 // head.  Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  When
 // H is a multiple of 8, XCD x owns the heads [x H/8, (x+1) H/8) of every batch entry (a GQA

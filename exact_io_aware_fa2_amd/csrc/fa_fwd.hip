@@ -60,11 +60,12 @@ __device__ __forceinline__ uint32_t word(const uint4& u, int m) {
 // accumulator layout of S^T) sit next to each other and load as one 16-byte read.
 __device__ __forceinline__ int vt_pos(int k) { return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1); }
 
-template <int D>
+template <int D, int AL>
 __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
     const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
     bf16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Nmax,
-    int causal, int window, float c, int neg_q, const int* __restrict__ cu, int ntot) {
+    int causal, int window, float c, int neg_q, const int* __restrict__ cu, int ntot,
+    const float* __restrict__ slopes) {
   using Cfg = FwdCfg<D>;
   constexpr int NT = Cfg::NT, BM = Cfg::BM, BN = Cfg::BN, KSTR = Cfg::KSTR, VSTR = Cfg::VSTR;
   constexpr int NC = D / 16;  // k-steps of S^T over the head dim
@@ -81,6 +82,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   seq_span(cu, ntot, b, Nmax, seq0, N);
   if (mb * BM >= N) return;  // a row block past the end of a shorter packed sequence
   const size_t lse0 = stat_base(cu, ntot, b, Hq, hq, Nmax, seq0);
+  const float slope2 = AL != 0 ? slopes[hq] * kLog2e : 0.f;
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int hh = lane >> 5, l32 = lane & 31;
@@ -202,14 +204,34 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   const int klo = window > 0 ? row - window + 1 : 0;  // allowed keys of this row: [klo, khi]
   const int khi = causal ? min(row, N - 1) : N - 1;
 
-  if (nb_lo < nb_hi) {
-    gload(nb_lo);
+  // Tile order.  Without a position bias: ascending.  With one, a row's largest biased
+  // scores sit near its diagonal, so the tiles are visited from there outwards and the
+  // reference max is set by the first tile instead of moving (and rescaling) on every one:
+  // causal, descending from the last tile (each wave's first active tile holds its
+  // diagonal); otherwise zig-zag outwards from the tile of the block's middle row.
+  const int ntiles = nb_hi - nb_lo;
+  const int nd = min(max((m0 + BM / 2) / BN, nb_lo), max(nb_hi - 1, nb_lo));
+  const int zl = nd - nb_lo, zu = nb_hi - 1 - nd, zm = min(zl, zu);
+  auto tile = [&](int t) {
+    if constexpr (AL == 0) {
+      return nb_lo + t;
+    } else if constexpr (AL == 1) {
+      return nb_hi - 1 - t;
+    } else {
+      if (t <= 2 * zm) return nd + ((t & 1) ? (t + 1) / 2 : -(t / 2));
+      return zu > zl ? nd + (t - zm) : nd - (t - zm);
+    }
+  };
+
+  if (ntiles > 0) {
+    gload(tile(0));
     swrite(0);
-    if (nb_lo + 1 < nb_hi) gload(nb_lo + 1);
+    if (ntiles > 1) gload(tile(1));
   }
   __syncthreads();
-  for (int nb = nb_lo; nb < nb_hi; ++nb) {
-    const int buf = (nb - nb_lo) & 1;
+  for (int t = 0; t < ntiles; ++t) {
+    const int nb = tile(t);
+    const int buf = t & 1;
     const bf16_t* sK = lds + buf * Cfg::BUF_ELEMS;
     const bf16_t* sV = sK + Cfg::K_ELEMS;
     const int n0 = nb * BN;
@@ -269,16 +291,30 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
           for (int i = 0; i < 8; ++i) q[i] = x[2 * i] + x[2 * i + 1];
           return ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
         };
+        // distance base of the piece for the position bias: key - row of element 0 of this
+        // lane half is k0 + 4 hh - row; element r adds 8 (r / 4) + r % 4
+        const float dbase = AL != 0 ? (float)(k0 + 4 * hh - row) : 0.f;
+        auto koff = [](int r) { return (float)(8 * (r >> 2) + (r & 3)); };
         float e[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(s[r], c, -m_i));  // 0 if masked
+        for (int r = 0; r < 16; ++r)  // 0 if masked
+          e[r] = fast_exp2(fmaf(s[r], c, alibi_addend<AL>(slope2, dbase, koff(r), m_i)));
         float rse = tree_sum(e);
         if (__any(!(rse <= kSumLimit))) {  // wave-uniform; rare after a row's first piece
-          float mx = fmaxf(s[0], s[1]);
+          float mt;
+          if constexpr (AL == 0) {
+            float mx = fmaxf(s[0], s[1]);
 #pragma unroll
-          for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);  // v_max3
-          mx = half_max(mx);
-          const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+            for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, s[r]), s[r + 1]);  // v_max3
+            mx = half_max(mx);
+            mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+          } else {  // the maximum of the biased scores
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              mx = fmaxf(mx, fmaf(s[r], c, alibi_addend<AL>(slope2, dbase, koff(r), 0.f)));
+            mt = half_max(mx);
+          }
           const bool grow = mt > m_i + kRescaleThreshold;
           const float alpha = grow ? fast_exp2(m_i - mt) : 1.f;  // 0 when m_i was -inf
           l_i *= alpha;
@@ -290,7 +326,8 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
           m_i = grow ? mt : m_i;
           const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(s[r], c, -m_use));
+          for (int r = 0; r < 16; ++r)
+            e[r] = fast_exp2(fmaf(s[r], c, alibi_addend<AL>(slope2, dbase, koff(r), m_use)));
           rse = tree_sum(e);
         }
         bf16x8 pp[2];
@@ -316,9 +353,9 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
         __builtin_amdgcn_s_setprio(0);
       }
     }
-    if (nb + 1 < nb_hi) {
+    if (t + 1 < ntiles) {
       swrite(buf ^ 1);
-      if (nb + 2 < nb_hi) gload(nb + 2);
+      if (t + 2 < ntiles) gload(tile(t + 2));
     }
     __syncthreads();
   }
@@ -442,12 +479,12 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(
 }
 
 // ---------------------------------------------------------------------------------
-template <int D>
+template <int D, int AL>
 static hipError_t launch_fwd_bf16_d(const FwdArgs& a, hipStream_t st) {
   using Cfg = FwdCfg<D>;
   static bool attr_done = false;
   if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D>,
+    hipError_t e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D, AL>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        Cfg::LDS_BYTES);
     if (e != hipSuccess) return e;
@@ -455,18 +492,24 @@ static hipError_t launch_fwd_bf16_d(const FwdArgs& a, hipStream_t st) {
   }
   const int num_m = (a.N + Cfg::BM - 1) / Cfg::BM;
   const int grid = a.B * a.Hq * num_m;
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(grid), dim3(Cfg::NT), Cfg::LDS_BYTES, st,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, AL>), dim3(grid), dim3(Cfg::NT), Cfg::LDS_BYTES, st,
                      (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (bf16_t*)a.o,
                      a.lse, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window, a.c_log2, a.neg_q, a.cu,
-                     a.ntot);
+                     a.ntot, a.slopes);
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_fwd_bf16_al(const FwdArgs& a, hipStream_t st) {
+  if (a.slopes == nullptr) return launch_fwd_bf16_d<D, 0>(a, st);
+  return a.causal ? launch_fwd_bf16_d<D, 1>(a, st) : launch_fwd_bf16_d<D, 2>(a, st);
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
   switch (a.d) {
-    case 64: return launch_fwd_bf16_d<64>(a, st);
-    case 128: return launch_fwd_bf16_d<128>(a, st);
-    case 256: return launch_fwd_bf16_d<256>(a, st);
+    case 64: return launch_fwd_bf16_al<64>(a, st);
+    case 128: return launch_fwd_bf16_al<128>(a, st);
+    case 256: return launch_fwd_bf16_al<256>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

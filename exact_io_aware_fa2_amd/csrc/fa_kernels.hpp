@@ -22,6 +22,7 @@ struct FwdArgs {
   const int* cu;        // packed sequences: B + 1 row offsets (device); null: fixed length
   int ntot;             // packed sequences: rows of the packed tensors
   float o_scale;        // E4M3 forward: the value factor, applied to O in the epilogue
+  const float* slopes;  // ALiBi slope per query head (device), or null for no position bias
 };
 
 struct BwdArgs {
@@ -42,6 +43,7 @@ struct BwdArgs {
   hipEvent_t ev_stop;
   const int* cu;        // packed sequences: B + 1 row offsets (device); null: fixed length
   int ntot;             // packed sequences: rows of the packed tensors
+  const float* slopes;  // ALiBi slope per query head (device), or null for no position bias
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);

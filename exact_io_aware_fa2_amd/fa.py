@@ -46,7 +46,7 @@ def load() -> ctypes.CDLL:
                            "`python -m exact_io_aware_fa2_amd.build` (no fallback exists)")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp]
     lib.fa_fwd.restype = i
     lib.fa_fwd_fp32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp32.restype = i
@@ -54,14 +54,15 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_fp8.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
-    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp,
+                           vp]
     lib.fa_bwd.restype = i
-    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_bwd_varlen_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd_varlen_workspace_size.restype = sz
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
-                                  i, f, vp, sz, vp]
+                                  i, f, vp, sz, vp, vp]
     lib.fa_bwd_varlen.restype = i
     lib.fa_bwd_time_main_kernel.argtypes = [vp, vp]
     lib.fa_bwd_time_main_kernel.restype = i
@@ -97,9 +98,11 @@ def _check(status: int):
 
 
 # ------------------------------------------------------------ 1:1 C entry points
-def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, stream=None) -> int:
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, stream=None,
+           alibi_slopes=None) -> int:
     return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
-                         int(causal), int(window), float(scale), _stream(stream))
+                         int(causal), int(window), float(scale), _ptr(alibi_slopes),
+                         _stream(stream))
 
 
 def fa_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, B, Hq, Hkv, N, d, causal,
@@ -119,17 +122,18 @@ def fa_bwd_workspace_size(B, Hq, Hkv, N, d, causal, window) -> int:
 
 
 def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
-           workspace, workspace_bytes, stream=None) -> int:
+           workspace, workspace_bytes, stream=None, alibi_slopes=None) -> int:
     return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq),
                          _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal), int(window),
-                         float(scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
+                         float(scale), _ptr(workspace), int(workspace_bytes),
+                         _ptr(alibi_slopes), _stream(stream))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, total, max_seqlen, Hq, Hkv, d, causal,
-                  window, scale, stream=None) -> int:
+                  window, scale, stream=None, alibi_slopes=None) -> int:
     return load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
                                 num_seqs, total, max_seqlen, Hq, Hkv, d, int(causal),
-                                int(window), float(scale), _stream(stream))
+                                int(window), float(scale), _ptr(alibi_slopes), _stream(stream))
 
 
 def fa_bwd_varlen_workspace_size(total, Hq, Hkv, d) -> int:
@@ -137,11 +141,13 @@ def fa_bwd_varlen_workspace_size(total, Hq, Hkv, d) -> int:
 
 
 def fa_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, num_seqs, total, max_seqlen, Hq,
-                  Hkv, d, causal, window, scale, workspace, workspace_bytes, stream=None) -> int:
+                  Hkv, d, causal, window, scale, workspace, workspace_bytes, stream=None,
+                  alibi_slopes=None) -> int:
     return load().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), num_seqs, total,
                                 max_seqlen, Hq, Hkv, d, int(causal), int(window), float(scale),
-                                _ptr(workspace), int(workspace_bytes), _stream(stream))
+                                _ptr(workspace), int(workspace_bytes), _ptr(alibi_slopes),
+                                _stream(stream))
 
 
 def fa_bwd_time_main_kernel(start_event, stop_event) -> int:
@@ -179,7 +185,20 @@ def _shapes(q, k, v):
     return B, N, Hq, k.shape[2], d
 
 
-def forward(q, k, v, causal=False, window=0, scale=None, out=None, lse=None, stream=None):
+def _slopes(alibi_slopes, Hq):
+    """Check an optional ALiBi slope tensor: float32, contiguous, on the device, Hq values."""
+    if alibi_slopes is None:
+        return None
+    t = alibi_slopes
+    if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
+            or t.numel() != Hq):
+        raise ValueError(f"alibi_slopes must be a contiguous float32 device tensor of {Hq} "
+                         "slopes (one per query head)")
+    return t
+
+
+def forward(q, k, v, causal=False, window=0, scale=None, out=None, lse=None, stream=None,
+            alibi_slopes=None):
     """O, LSE = attention(q, k, v); bf16 or fp32 tensors in [B, N, H, d] layout."""
     B, N, Hq, Hkv, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -188,8 +207,11 @@ def forward(q, k, v, causal=False, window=0, scale=None, out=None, lse=None, str
     if lse is None:
         lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
     if q.dtype == torch.bfloat16:
-        _check(fa_fwd(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, stream))
+        _check(fa_fwd(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, stream,
+                      _slopes(alibi_slopes, Hq)))
     elif q.dtype == torch.float32:
+        if alibi_slopes is not None:
+            raise ValueError("the float32 forward has no position bias")
         _check(fa_fwd_fp32(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, stream))
     else:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -222,7 +244,7 @@ def workspace_for(B, Hq, Hkv, N, d, causal, window, device) -> torch.Tensor:
 
 
 def backward(q, k, v, o, dO, lse, causal=False, window=0, scale=None, dq=None, dk=None,
-             dv=None, workspace=None, stream=None):
+             dv=None, workspace=None, stream=None, alibi_slopes=None):
     """dQ, dK, dV of L = sum(O * dO) for bf16 tensors."""
     B, N, Hq, Hkv, d = _shapes(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -232,7 +254,8 @@ def backward(q, k, v, o, dO, lse, causal=False, window=0, scale=None, dq=None, d
     if workspace is None:
         workspace = workspace_for(B, Hq, Hkv, N, d, causal, window, q.device)
     _check(fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
-                  workspace, workspace.numel() * workspace.element_size(), stream))
+                  workspace, workspace.numel() * workspace.element_size(), stream,
+                  _slopes(alibi_slopes, Hq)))
     return dq, dk, dv
 
 
@@ -257,14 +280,14 @@ def _shapes_varlen(q, k, v, cu_seqlens):
 
 
 def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, scale=None,
-                   out=None, lse=None, stream=None):
+                   out=None, lse=None, stream=None, alibi_slopes=None):
     """O [total, Hq, d], LSE [Hq, total] for packed bf16 sequences."""
     T, Hq, Hkv, d, S = _shapes_varlen(q, k, v, cu_seqlens)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((Hq, T), device=q.device, dtype=torch.float32) if lse is None else lse
     _check(fa_fwd_varlen(q, k, v, out, lse, cu_seqlens, S, T, max_seqlen, Hq, Hkv, d, causal,
-                         window, scale, stream))
+                         window, scale, stream, _slopes(alibi_slopes, Hq)))
     return out, lse
 
 
@@ -276,7 +299,8 @@ def workspace_for_varlen(total, Hq, Hkv, d, device) -> torch.Tensor:
 
 
 def backward_varlen(q, k, v, o, dO, lse, cu_seqlens, max_seqlen, causal=False, window=0,
-                    scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+                    scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
+                    alibi_slopes=None):
     """dQ, dK, dV of L = sum(O * dO) for packed bf16 sequences."""
     T, Hq, Hkv, d, S = _shapes_varlen(q, k, v, cu_seqlens)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
@@ -287,5 +311,6 @@ def backward_varlen(q, k, v, o, dO, lse, cu_seqlens, max_seqlen, causal=False, w
         workspace = workspace_for_varlen(T, Hq, Hkv, d, q.device)
     _check(fa_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, S, T, max_seqlen, Hq, Hkv,
                          d, causal, window, scale, workspace,
-                         workspace.numel() * workspace.element_size(), stream))
+                         workspace.numel() * workspace.element_size(), stream,
+                         _slopes(alibi_slopes, Hq)))
     return dq, dk, dv

@@ -35,6 +35,7 @@ class Workload:
     sigma_do: float = 1.0
     backward: bool = True
     seed: int = 1000
+    alibi: bool = False  # position bias with alibi_slopes(Hq)
 
     @property
     def scale(self) -> float:
@@ -66,6 +67,18 @@ WORKLOADS = {
 }
 
 HEADLINE = "bf16_b2_h32_n8192_d128_causal"
+
+def alibi_slopes(h: int) -> list:
+    """The geometric slope set of the ALiBi method: head i (1-based) of h gets 2^(-8 i / h)."""
+    return [2.0 ** (-8.0 * i / h) for i in range(1, h + 1)]
+
+
+# The bench workload with the ALiBi position bias (the geometric slopes above).
+ALIBI_WORKLOADS = {
+    "bf16_b2_h32_n8192_d128_causal_alibi": Workload(
+        "bf16_b2_h32_n8192_d128_causal_alibi", "bf16", 2, 32, 32, 8192, 128, True, seed=1007,
+        alibi=True),
+}
 
 # The bench workload's shape with 8-bit E4M3 inputs (forward only).
 FP8_WORKLOADS = {

@@ -25,6 +25,14 @@
  *   window == 0 : no window
  * A masked entry has probability zero: it never enters the normaliser.
  *
+ * Position bias (bmjup.com page, FAQ on inference: the alibi_slopes argument, no bias when
+ * it is None; hysenlabs.com page, hardware-boundary section: ALiBi): fa_fwd, fa_bwd,
+ * fa_fwd_varlen and fa_bwd_varlen take `alibi_slopes`, NULL for none or a device array of
+ * Hq float32 slopes m_h (caller-owned, read by the kernels only, used as given, any finite
+ * value).  Query head h then scores s_ij = scale * q_i . k_j - m_h * |i - j| before the
+ * mask and the softmax, with positions counted from the start of each sequence; lse is
+ * the logsumexp of those biased scores, and the backward treats the slopes as constants.
+ *
  * Conventions for every entry point:
  *   - The caller owns every buffer (device memory, e.g. from hipMalloc or a framework
  *     allocator).  The library never allocates, frees or synchronises.
@@ -64,7 +72,7 @@ typedef enum {
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int Hq, int Hkv, int N, int d, int causal, int window, float scale,
-                 void* stream);
+                 const float* alibi_slopes, void* stream);
 
 /*
  * Forward with 8-bit inputs.  The pages name an FP8 forward pass of a later version of the
@@ -124,7 +132,7 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, i
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
                  int N, int d, int causal, int window, float scale, void* workspace,
-                 size_t workspace_bytes, void* stream);
+                 size_t workspace_bytes, const float* alibi_slopes, void* stream);
 
 /*
  * Packed variable-length sequences.  bmjup.com, "FlashAttention-2 ... 实战解析", FAQ Q4,
@@ -148,7 +156,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  */
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
-                        int Hkv, int d, int causal, int window, float scale, void* stream);
+                        int Hkv, int d, int causal, int window, float scale,
+                        const float* alibi_slopes, void* stream);
 
 /* Workspace bytes for fa_bwd_varlen: D as float32 [Hq, total] rounded up to 256; 0 for
  * invalid sizes. */
@@ -158,7 +167,7 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         const void* dO, const float* lse, void* dq, void* dk, void* dv,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
                         int Hkv, int d, int causal, int window, float scale, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        size_t workspace_bytes, const float* alibi_slopes, void* stream);
 
 /*
  * Benchmark hook (no counterpart on the pages): the next fa_bwd (or fa_bwd_varlen) call made on this thread
