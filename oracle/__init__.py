@@ -42,5 +42,6 @@ from .attention import (  # noqa: F401
     attended_pairs,
     attn_fwd_varlen,
     attn_bwd_varlen,
+    attn_decode,
 )
 from .fp8 import attn_fwd_fp8, attn_fwd_fp8_rows, dequantize, e4m3_decode  # noqa: F401

@@ -448,3 +448,52 @@ def attn_bwd_varlen(q, k, v, do, cu_seqlens, causal=False, window=0, scale=None,
             dv[s0:s1, h // g] += dvh
             dvec[h, s0:s1] = dh
     return dq, dk, dv, dvec
+
+
+# ------------------------------------------------------------------ decoding over a cache
+def attn_decode(q, k_cache, v_cache, seqlens_k=None, causal=True, window=0, scale=None):
+    """Attention of the newest queries of each sequence over its cached keys.
+
+    q [B, Nq, Hq, d]: the Nq newest tokens; k_cache, v_cache [B, Nk, Hkv, d]: the cache,
+    of which sequence b uses the first seqlens_k[b] rows (all Nk when None).  Query i of
+    sequence b sits at position len_b - Nq + i (the queries are the sequence's last Nq
+    positions), and the causal and window masks count from there; without the causal mask
+    every query sees all len_b keys (the window still bounds from the left).  This is plain
+    attention over the cache for the pages' use in inference (bmjup.com, FAQ on inference:
+    streaming generation and large context caches).  Returns O [B, Nq, Hq, dv] and
+    LSE [B, Hq, Nq]; a query with no allowed key gets O = 0 and LSE = -inf.
+    """
+    q, k_cache, v_cache = _as64(q), _as64(k_cache), _as64(v_cache)
+    b, nq, hq, d = q.shape
+    nk, hkv = k_cache.shape[1], k_cache.shape[2]
+    if hq % hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    lens = np.full(b, nk) if seqlens_k is None else np.asarray(seqlens_k, dtype=np.int64)
+    if lens.shape != (b,) or np.any(lens < 0) or np.any(lens > nk):
+        raise ValueError("seqlens_k must hold one length in [0, Nk] per sequence")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    g = hq // hkv
+    o = np.zeros((b, nq, hq, v_cache.shape[3]))
+    lse = np.full((b, hq, nq), -np.inf)
+    for bi in range(b):
+        n = int(lens[bi])
+        pos = n - nq + np.arange(nq)          # positions of the queries
+        j = np.arange(n)[None, :]
+        ok = np.ones((nq, n), dtype=bool)
+        if causal:
+            ok &= j <= pos[:, None]
+        if window > 0:
+            ok &= j >= pos[:, None] - window + 1
+        for h in range(hq):
+            s = scale * (q[bi, :, h] @ k_cache[bi, :n, h // g].T)
+            s = np.where(ok, s, -np.inf)
+            m = s.max(axis=1) if n > 0 else np.full(nq, -np.inf)
+            fin = np.isfinite(m)
+            m0 = np.where(fin, m, 0.0)
+            e = np.exp(s - m0[:, None])
+            den = e.sum(axis=1)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                p = np.where(fin[:, None], e / np.where(fin, den, 1.0)[:, None], 0.0)
+                lse[bi, h] = np.where(fin, m0 + np.log(np.where(fin, den, 1.0)), -np.inf)
+            o[bi, :, h] = p @ v_cache[bi, :n, h // g]
+    return o, lse

@@ -689,3 +689,64 @@ def test_alibi_packed_positions_start_at_each_sequence():
                   do.reshape(nb, n, hq, d), True, 0, 0.5, alibi_slopes=sl)
     for a, bt in zip(g[:3], gb[:3]):
         np.testing.assert_array_equal(a, bt.reshape(a.shape))
+
+
+# ------------------------------------------------------------------ decoding over a cache
+@pytest.mark.parametrize("causal,window", [(True, 0), (True, 5), (False, 0), (False, 7)])
+def test_decode_equals_last_rows_of_full_attention(causal, window):
+    """Decoding the last Nq queries against the whole sequence's keys is the last Nq rows
+    of ordinary attention over that sequence (the batched oracle)."""
+    from oracle import attn_decode
+    rng = np.random.default_rng(60)
+    b, n, nq, hq, hkv, d = 2, 29, 3, 4, 2, 8
+    q, k, v = (rng.standard_normal((b, n, h, d)) for h in (hq, hkv, hkv))
+    o_full, lse_full = attn_fwd(q, k, v, causal, window, 0.4)
+    o, lse = attn_decode(q[:, n - nq:], k, v, None, causal, window, 0.4)
+    np.testing.assert_allclose(o, o_full[:, n - nq:], atol=1e-13)
+    np.testing.assert_allclose(lse, lse_full[:, :, n - nq:], atol=1e-13)
+
+
+def test_decode_per_sequence_lengths_and_unused_cache_rows():
+    from oracle import attn_decode
+    rng = np.random.default_rng(61)
+    b, nk, nq, hq, hkv, d = 3, 20, 2, 2, 1, 4
+    q = rng.standard_normal((b, nq, hq, d))
+    k, v = rng.standard_normal((b, nk, hkv, d)), rng.standard_normal((b, nk, hkv, d))
+    lens = [20, 7, 1]
+    o, lse = attn_decode(q, k, v, lens, True, 0, 0.5)
+    k2, v2 = k.copy(), v.copy()
+    k2[1, 7:] = 1e3  # rows past a sequence's length are never read
+    v2[1, 7:] = np.nan
+    o2, lse2 = attn_decode(q, k2, v2, lens, True, 0, 0.5)
+    np.testing.assert_array_equal(o, o2)
+    for bi, n in enumerate(lens):
+        o_full, lse_full = attn_fwd(np.concatenate([np.zeros((1, n - nq, hq, d)) if n >= nq else
+                                                    np.zeros((1, 0, hq, d)),
+                                                    q[bi:bi + 1, max(0, nq - n):]], axis=1),
+                                    k[bi:bi + 1, :n], v[bi:bi + 1, :n], True, 0, 0.5)
+        if n >= nq:
+            np.testing.assert_allclose(o[bi], o_full[0, n - nq:], atol=1e-13)
+    # sequence 2 has one key and two queries: query 0 sits at position -1 and sees nothing
+    assert np.all(o[2, 0] == 0) and np.all(np.isneginf(lse[2, :, 0]))
+    np.testing.assert_allclose(o[2, 1], np.repeat(v[2, 0], hq // hkv, axis=0), atol=1e-15)
+
+
+def test_decode_matches_torch_sdpa_with_explicit_mask():
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    from oracle import attn_decode
+    rng = np.random.default_rng(62)
+    b, nk, nq, hq, hkv, d = 1, 40, 4, 4, 2, 8
+    q = rng.standard_normal((b, nq, hq, d))
+    k, v = rng.standard_normal((b, nk, hkv, d)), rng.standard_normal((b, nk, hkv, d))
+    o, lse = attn_decode(q, k, v, [33], True, 9, 0.3)
+    pos = torch.arange(33 - nq, 33)[:, None]
+    j = torch.arange(33)[None, :]
+    ok = (j <= pos) & (j >= pos - 8)
+    tq = torch.tensor(q).transpose(1, 2)
+    tk = torch.tensor(k[:, :33]).transpose(1, 2).repeat_interleave(2, dim=1)
+    tv = torch.tensor(v[:, :33]).transpose(1, 2).repeat_interleave(2, dim=1)
+    ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=ok, scale=0.3)
+    np.testing.assert_allclose(o, ref.transpose(1, 2).numpy(), atol=1e-13)
+    s = (tq @ tk.transpose(-1, -2) * 0.3).masked_fill(~ok, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), atol=1e-13)
