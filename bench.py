@@ -176,6 +176,146 @@ def cpu_baseline(w, q, k, v, do, packed=False, max_workers: int = 16):
     }
 
 
+def _decode_task(args):
+    import oracle.attention as oa
+    q, k, v, n, causal, window, scale = args
+    return oa.attn_decode(q, k, v, [n], causal, window, scale)
+
+
+def cpu_baseline_decode(w, q, k, v, flop_per_seq, max_workers: int = 16):
+    """The float64 oracle's attn_decode, one task per sequence, on the host cores."""
+    import numpy as np
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
+    import oracle.attention as oa
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    workers = max(1, min(max_workers, cores, w.B))
+    f64 = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    tasks = [(f64(q[b:b + 1]), f64(k[b:b + 1, :n]), f64(v[b:b + 1, :n]), n, w.causal, w.window,
+              w.scale) for b, n in enumerate(w.lens)]
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx,
+                             initializer=oa._limit_blas_threads) as ex:
+        list(ex.map(oa.default_workers, range(workers)))
+        t0 = time.perf_counter()
+        list(ex.map(_decode_task, tasks))
+        dt = time.perf_counter() - t0
+    return {
+        "value": sum(flop_per_seq) / dt / 1e12,
+        "unit": "TFLOP/s (decode, algorithmic)",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"all {w.B} sequences of {w.name}, float64 NumPy attn_decode, {workers} worker "
+                  f"processes x 1 BLAS thread, {dt:.1f} s wall",
+        "seconds": dt,
+    }
+
+
+def decode_bytes_and_flop(w):
+    """Algorithmic HBM bytes and flop of one decoding step: each sequence's K and V rows that
+    some query may attend, read once per KV head, plus q, o (bf16) and lse (float32)."""
+    total_b, flops = 0, []
+    for n in w.lens:
+        pos = [n - w.Nq + i for i in range(w.Nq)]
+        lo = max(0, n - w.Nq - w.window + 1) if w.window > 0 else 0
+        keys = max(0, n - lo)
+        total_b += keys * w.Hkv * w.d * 2 * 2
+        pairs = 0
+        for p in pos:
+            hi = min(n, p + 1) if w.causal else n
+            l0 = max(0, p - w.window + 1) if w.window > 0 else 0
+            pairs += max(0, hi - l0)
+        flops.append(4.0 * w.d * w.Hq * pairs)
+    total_b += w.B * w.Nq * w.Hq * w.d * 2 * 2 + w.B * w.Hq * w.Nq * 4
+    return total_b, flops
+
+
+def run_decode(args, w):
+    import torch
+    from exact_io_aware_fa2_amd import fa
+    from exact_io_aware_fa2_amd.workloads import make_decode_inputs
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    q, k, v, sl = make_decode_inputs(w, dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.Hq, w.Nq), device=dev, dtype=torch.float32)
+    S = fa.fa_decode_num_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, 0)
+    nbytes = fa.fa_decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, S)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def step():
+        st = fa.fa_decode(q, k, v, sl, o, lse, w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal,
+                          w.window, w.scale, S, ws, nbytes, sh)
+        if st != fa.FA_OK:
+            raise RuntimeError(fa.fa_last_error())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for e in ev:
+        e[2].record(stream)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(K):
+        e = ev[s_]
+        fa.fa_bwd_time_main_kernel(e[2], e[3])  # events around the chunk kernel
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    kern_ms = [e[2].elapsed_time(e[3]) for e in ev]
+    avg = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
+    nb, flops = decode_bytes_and_flop(w)
+    F = sum(flops)
+    ms_step = wall * 1e3 / K
+    km = avg(kern_ms)
+    out = {
+        "metric": "attention fwd & fwd+bwd TFLOPs/s (bf16, d=128, N=8K causal); % of MFMA peak",
+        "value": F / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s (decode step, algorithmic)",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 1) draws, rounded to bf16)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq,
+                   "Nk": w.Nk, "d": w.d, "causal": w.causal, "window": w.window,
+                   "num_splits": S, "scale": w.scale},
+        "tokens_per_s": w.B * w.Nq / (ms_step * 1e-3),
+        "decode_call_ms": avg(call_ms),
+        "kernel_ms": {"decode_call": {"mean": avg(call_ms), "median": med(call_ms),
+                                      "min": min(call_ms)},
+                      "decode_kernel": {"mean": km, "median": med(kern_ms), "min": min(kern_ms)}},
+        "roofline": {"kernel": "decode_kernel", "bound": "hbm", "achieved": nb / (km * 1e-3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": nb / (km * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": _traffic("decode_kernel", w.name, "fa_decode.hip"),
+                     "algorithmic_bytes": nb, "avg_launch_ms": km},
+    }
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = src.numel()
+        del src, dst
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w, q, k, v, flops)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -193,6 +333,10 @@ def main() -> int:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                           "(the hot path shards over (batch, head) pairs, see DESIGN.md)"}))
         return 2
+
+    from exact_io_aware_fa2_amd.workloads import DECODE_WORKLOADS
+    if args.workload in DECODE_WORKLOADS:
+        return run_decode(args, DECODE_WORKLOADS[args.workload])
 
     import torch
     from exact_io_aware_fa2_amd import fa

@@ -4,6 +4,8 @@
 // allocates or synchronises, and reports failures through a status code plus a
 // thread-local message.
 #include <math.h>
+
+#include <algorithm>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -35,6 +37,7 @@ fa_status ok() {
 }
 
 constexpr int64_t kMaxElems = (int64_t)1 << 31;  // kernels index rows with 32-bit ints
+constexpr int kMaxSplits = 256;                  // key chunks per sequence in fa_decode
 
 fa_status check_common(const char* fn, int B, int Hq, int Hkv, int N, int d, int causal,
                        int window, float scale) {
@@ -219,6 +222,83 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
   g_time_start = g_time_stop = nullptr;
   a.slopes = alibi_slopes;
   return launched("fa_bwd_varlen", fa::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || Hq % Hkv != 0 ||
+      (d != 64 && d != 128) || num_splits < 0 || num_splits > kMaxSplits)
+    return 0;
+  if (num_splits > 0) return num_splits;
+  // Enough workgroups for two per compute unit on 256 units, chunks of at least 256 keys.
+  const long nrg = ((long)(Hq / Hkv) * Nq + 31) / 32;
+  const long base = (long)B * Hkv * nrg;
+  long s = (512 + base - 1) / base;
+  s = std::min<long>(s, std::max(1, Nk / 256));
+  s = std::min<long>(s, 64);
+  return (int)std::max<long>(s, 1);
+}
+
+size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  const int S = fa_decode_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits);
+  if (S <= 1) return 0;
+  const size_t rows = (size_t)S * B * Hq * Nq;
+  return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
+}
+
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int* seqlens_k, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                    int Nk, int d, int causal, int window, float scale, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !o || !lse)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode: null pointer");
+  if (Nq <= 0) return fail(FA_ERR_INVALID_ARG, "fa_decode: Nq=%d must be positive", Nq);
+  fa_status st = check_common("fa_decode", B, Hq, Hkv, Nk, d, causal, window, scale);
+  if (st != FA_OK) return st;
+  if (d != 64 && d != 128)
+    return fail(FA_ERR_UNSUPPORTED, "fa_decode: head dim %d not supported (64 or 128)", d);
+  if ((int64_t)B * Nq * Hq * d >= kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode: B*Nq*Hq*d exceeds 2^31");
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode: num_splits=%d outside [0, %d]", num_splits,
+                kMaxSplits);
+  const int S = fa_decode_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits);
+  if ((int64_t)B * Hkv * ((Hq / Hkv * Nq + 31) / 32) * S >= kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode: grid too large");
+  const size_t need = fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FA_ERR_WORKSPACE, "fa_decode: workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && ((uintptr_t)workspace & 255) != 0)
+    return fail(FA_ERR_WORKSPACE, "fa_decode: workspace must be 256-byte aligned");
+  const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;  // as in fa_fwd
+  fa::DecodeArgs a{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.seqlens = seqlens_k;
+  a.o = o;
+  a.lse = lse;
+  if (S > 1) {
+    const size_t rows = (size_t)S * B * Hq * Nq;
+    a.opart = static_cast<float*>(workspace);
+    a.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       align256(rows * d * sizeof(float)));
+  }
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.causal = causal ? 1 : 0;
+  a.window = window;
+  a.c_log2 = c2;
+  a.neg_q = scale < 0.f ? 1 : 0;
+  a.S = S;
+  a.ev_start = g_time_start;
+  a.ev_stop = g_time_stop;
+  g_time_start = g_time_stop = nullptr;
+  return launched("fa_decode", fa::launch_decode(a, (hipStream_t)stream));
 }
 
 fa_status fa_bwd_time_main_kernel(void* start_event, void* stop_event) {

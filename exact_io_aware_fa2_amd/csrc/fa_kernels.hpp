@@ -46,7 +46,25 @@ struct BwdArgs {
   const float* slopes;  // ALiBi slope per query head (device), or null for no position bias
 };
 
+struct DecodeArgs {
+  const void* q;        // [B, Nq, Hq, d] bf16
+  const void* k;        // [B, Nk, Hkv, d] bf16 cache
+  const void* v;
+  const int* seqlens;   // [B] cached lengths (device), or null: all Nk
+  void* o;              // [B, Nq, Hq, d] bf16
+  float* lse;           // [B, Hq, Nq]
+  float* opart;         // S > 1: [S, B, Hq, Nq, d] float32 partial outputs
+  float* lpart;         // S > 1: [S, B, Hq, Nq] partial logsumexps (log2 units)
+  int B, Hq, Hkv, Nq, Nk, d, causal, window;
+  float c_log2;         // |scale| * log2(e)
+  int neg_q;
+  int S;                // key chunks per sequence
+  hipEvent_t ev_start;  // optional events recorded around the chunk kernel (may be null)
+  hipEvent_t ev_stop;
+};
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t st);
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);

@@ -21,7 +21,8 @@ _lib = None
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_varlen",
+EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_decode", "fa_decode_num_splits",
+            "fa_decode_workspace_size", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_varlen",
             "fa_bwd_varlen", "fa_bwd_varlen_workspace_size", "fa_bwd_time_main_kernel",
             "fa_mfma_probe", "fa_last_error", "fa_version")
 
@@ -64,6 +65,12 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
                                   i, f, vp, sz, vp, vp]
     lib.fa_bwd_varlen.restype = i
+    lib.fa_decode_num_splits.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_decode_num_splits.restype = i
+    lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.fa_decode_workspace_size.restype = sz
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_decode.restype = i
     lib.fa_bwd_time_main_kernel.argtypes = [vp, vp]
     lib.fa_bwd_time_main_kernel.restype = i
     lib.fa_mfma_probe.argtypes = [vp, i, i, vp]
@@ -148,6 +155,22 @@ def fa_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, num_seqs, total, 
                                 max_seqlen, Hq, Hkv, d, int(causal), int(window), float(scale),
                                 _ptr(workspace), int(workspace_bytes), _ptr(alibi_slopes),
                                 _stream(stream))
+
+
+def fa_decode_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
+    return load().fa_decode_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits)
+
+
+def fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
+    return load().fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
+
+
+def fa_decode(q, k_cache, v_cache, seqlens_k, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, window,
+              scale, num_splits, workspace, workspace_bytes, stream=None) -> int:
+    return load().fa_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seqlens_k), _ptr(o),
+                            _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(causal), int(window),
+                            float(scale), int(num_splits), _ptr(workspace),
+                            int(workspace_bytes), _stream(stream))
 
 
 def fa_bwd_time_main_kernel(start_event, stop_event) -> int:
@@ -314,3 +337,31 @@ def backward_varlen(q, k, v, o, dO, lse, cu_seqlens, max_seqlen, causal=False, w
                          workspace.numel() * workspace.element_size(), stream,
                          _slopes(alibi_slopes, Hq)))
     return dq, dk, dv
+
+
+def decode(q, k_cache, v_cache, seqlens_k=None, causal=True, window=0, scale=None,
+           num_splits=0, out=None, lse=None, workspace=None, stream=None):
+    """O [B, Nq, Hq, d] (bf16), LSE [B, Hq, Nq] of the newest Nq queries over a bf16 KV
+    cache [B, Nk, Hkv, d]; seqlens_k: int32 device tensor [B] or None (all Nk)."""
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q [B, Nq, Hq, d] and caches [B, Nk, Hkv, d] expected")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError(f"shape mismatch q={tuple(q.shape)} cache={tuple(k_cache.shape)}")
+    for t in (q, k_cache, v_cache):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q and the caches must be contiguous bf16 device tensors")
+    if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B
+                                  or not seqlens_k.is_cuda):
+        raise ValueError("seqlens_k must be an int32 device tensor of B lengths")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32) if lse is None else lse
+    nbytes = fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(fa_decode(q, k_cache, v_cache, seqlens_k, out, lse, B, Hq, Hkv, Nq, Nk, d, causal,
+                     window, scale, num_splits, workspace, wbytes, stream))
+    return out, lse

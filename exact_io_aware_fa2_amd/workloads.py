@@ -231,3 +231,54 @@ def make_fp8_inputs(w: Workload, device: str | torch.device = "cpu"):
         out.append(c.to(device))
         factors.append(f)
     return out[0], out[1], out[2], tuple(factors)
+
+
+# ------------------------------------------------------------------ decoding over a cache
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq new tokens per sequence over a bf16 KV cache of Nk rows (lengths: the cached
+    length of each sequence, None for Nk everywhere)."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool = True
+    window: int = 0
+    lengths: tuple | None = None
+    seed: int = 3000
+    dtype: str = "bf16"
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+    @property
+    def lens(self) -> list:
+        return [self.Nk] * self.B if self.lengths is None else [int(n) for n in self.lengths]
+
+
+# One decoding step of 8 sequences with 32768 cached tokens each, grouped-query heads as in
+# the 65536-token workload (32 query heads over 8 KV heads), d = 128.
+DECODE_WORKLOADS = {
+    "bf16_decode_b8_hq32_hkv8_nq1_nk32768_d128": DecodeWorkload(
+        "bf16_decode_b8_hq32_hkv8_nq1_nk32768_d128", 8, 32, 8, 1, 32768, 128, seed=3001),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload, device: str | torch.device = "cpu"):
+    """(q [B, Nq, Hq, d], k_cache, v_cache [B, Nk, Hkv, d], seqlens int32 [B] or None),
+    drawn in the manner of make_inputs (order q, k, v)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(w.seed)
+
+    def draw(shape):
+        return torch.randn(shape, generator=g, dtype=torch.float32).to(torch.bfloat16).to(device)
+
+    q = draw((w.B, w.Nq, w.Hq, w.d))
+    k = draw((w.B, w.Nk, w.Hkv, w.d))
+    v = draw((w.B, w.Nk, w.Hkv, w.d))
+    lens = None if w.lengths is None else torch.tensor(w.lens, dtype=torch.int32).to(device)
+    return q, k, v, lens

@@ -170,10 +170,41 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         size_t workspace_bytes, const float* alibi_slopes, void* stream);
 
 /*
- * Benchmark hook (no counterpart on the pages): the next fa_bwd (or fa_bwd_varlen) call made on this thread
- * records `start_event` on its stream right before its key-block kernel (dK, dV) and
- * `stop_event` right after it (the query-block kernel for dQ follows), so a caller can time
- * the backward kernels separately with hipEventElapsedTime.  Arguments are hipEvent_t handles owned by the caller; passing NULL
+ * Decoding: the newest queries of each sequence over its KV cache, the method at inference
+ * over large context caches (bmjup.com, "FlashAttention-2 ... 实战解析", FAQ on inference).
+ *   q [B, Nq, Hq, d]        : bf16, the Nq newest tokens of each sequence
+ *   k_cache, v_cache        : bf16 [B, Nk, Hkv, d]; sequence b uses its first seqlens_k[b]
+ *                             rows
+ *   seqlens_k               : device int32 [B], or NULL for Nk everywhere; values are
+ *                             clamped into [0, Nk] by the kernels (not read on the host)
+ *   o [B, Nq, Hq, d] bf16, lse [B, Hq, Nq] float32 natural log
+ * Query i of sequence b sits at position seqlens_k[b] - Nq + i; causal and window masks
+ * count from there (without causal every query sees the whole cached sequence; a window
+ * still bounds from the left).  A query with no allowed key gets o = 0 and lse = -inf.
+ * The keys any query of a sequence may attend are split into num_splits chunks (0: the
+ * library chooses, see fa_decode_num_splits); each chunk's workgroups write a partial
+ * output and logsumexp to the workspace and a second kernel merges them exactly
+ * (LSE = ln sum e^LSE_s, O = sum e^(LSE_s - LSE) O_s).  With one chunk no workspace is
+ * used (it may be NULL).  d must be 64 or 128 (FA_ERR_UNSUPPORTED otherwise); Nq >= 1;
+ * num_splits in [0, 256].  Other rules as fa_fwd.
+ */
+int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
+
+/* Workspace bytes fa_decode needs for these sizes and num_splits (0 when one chunk or
+ * invalid sizes). */
+size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits);
+
+fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int* seqlens_k, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                    int Nk, int d, int causal, int window, float scale, int num_splits,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Benchmark hook (no counterpart on the pages): the next fa_bwd, fa_bwd_varlen or fa_decode
+ * call made on this thread records `start_event` on its stream right before its main kernel
+ * (the key-block kernel for dK, dV; the chunk kernel of fa_decode) and `stop_event` right
+ * after it (the dQ kernel, or the chunk merge, follows), so a caller can time the kernels
+ * separately with hipEventElapsedTime.  Arguments are hipEvent_t handles owned by the caller; passing NULL
  * for both clears a pending request.  Returns FA_ERR_INVALID_ARG if exactly one is NULL.
  */
 fa_status fa_bwd_time_main_kernel(void* start_event, void* stop_event);

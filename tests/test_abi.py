@@ -179,3 +179,38 @@ def test_fp8_forward_validation(bad, status):
     st = fa.fa_fwd_fp8(None, fake, fake, fake, fake, 1.0, 1.0, 1.0, 1, 1, 1, 8, 64, 0, 0, 0.1,
                        stream=0)
     assert st == fa.FA_ERR_INVALID_ARG and "null" in fa.fa_last_error()
+
+
+def test_decode_validation_and_splits():
+    fake = 256
+    base = dict(B=2, Hq=8, Hkv=2, Nq=1, Nk=4096, d=128)
+    ns = fa.fa_decode_num_splits(*base.values(), 0)
+    assert ns >= 1
+    assert fa.fa_decode_num_splits(*base.values(), 5) == 5
+    assert fa.fa_decode_num_splits(2, 8, 2, 1, 4096, 256, 0) == 0  # d = 256 unsupported
+    assert fa.fa_decode_workspace_size(*base.values(), 1) == 0
+    need = fa.fa_decode_workspace_size(*base.values(), 4)
+    rows = 4 * 2 * 8 * 1
+    assert need == ((rows * 128 * 4 + 255) // 256) * 256 + ((rows * 4 + 255) // 256) * 256
+
+    def call(**kw):
+        a = dict(base, causal=1, window=0, scale=0.1, num_splits=4, ws=4096, wsb=need)
+        a.update(kw)
+        return fa.fa_decode(fake, fake, fake, None, fake, fake, a["B"], a["Hq"], a["Hkv"],
+                            a["Nq"], a["Nk"], a["d"], a["causal"], a["window"], a["scale"],
+                            a["num_splits"], a["ws"], a["wsb"], stream=0)
+
+    assert call(Nq=0) == fa.FA_ERR_INVALID_ARG
+    assert call(Hq=6, Hkv=4) == fa.FA_ERR_INVALID_ARG
+    assert call(d=256) == fa.FA_ERR_UNSUPPORTED
+    assert call(num_splits=-1) == fa.FA_ERR_INVALID_ARG
+    assert call(num_splits=257) == fa.FA_ERR_INVALID_ARG
+    assert call(wsb=need - 1) == fa.FA_ERR_WORKSPACE
+    assert call(ws=4096 + 8) == fa.FA_ERR_WORKSPACE
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(window=-1) == fa.FA_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_last_error().startswith("fa_decode")
+    st = fa.fa_decode(None, fake, fake, None, fake, fake, 1, 1, 1, 1, 8, 64, 1, 0, 0.1, 1, None,
+                      0, stream=0)
+    assert st == fa.FA_ERR_INVALID_ARG and "null" in fa.fa_last_error()
