@@ -229,10 +229,11 @@ int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_
       (d != 64 && d != 128) || num_splits < 0 || num_splits > kMaxSplits)
     return 0;
   if (num_splits > 0) return num_splits;
-  // Enough workgroups for two per compute unit on 256 units, chunks of at least 256 keys.
+  // About one workgroup per compute unit (256 units; measured faster than two per unit,
+  // with a shorter merge), chunks of at least 256 keys.
   const long nrg = ((long)(Hq / Hkv) * Nq + 31) / 32;
   const long base = (long)B * Hkv * nrg;
-  long s = (512 + base - 1) / base;
+  long s = (256 + base - 1) / base;
   s = std::min<long>(s, std::max(1, Nk / 256));
   s = std::min<long>(s, 64);
   return (int)std::max<long>(s, 1);
