@@ -538,17 +538,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       // S = Q K^T and dP = dO V^T (lane = key, the step's 32 rows in registers).
       const bf16_t* qa = sQ + l32 * STR + 8 * hh;
       const bf16_t* oa = sO + l32 * STR + 8 * hh;
+      // The operands of k-step cc + 1 are read while k-step cc's products issue (two named
+      // buffers); the scheduling barrier after each k-step keeps later reads from being
+      // hoisted further, which would need more registers than two waves per SIMD leave.
       f32x16 s = zero16(), dp = zero16();
-      __builtin_amdgcn_s_setprio(1);
+      if constexpr (AL == 0) {
+        bf16x8 opq[2], opo[2], opv[2];
+        opq[0] = lds_read_b128(qa);
+        opo[0] = lds_read_b128(oa);
+        opv[0] = lds_read_b128(vp);
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        s = mfma32(lds_read_b128(qa + 16 * cc), kop[cc], s);
-        dp = mfma32(lds_read_b128(oa + 16 * cc), lds_read_b128(vp + 16 * cc), dp);
-        // keep the operand reads of later k-steps from being hoisted here: with two waves
-        // per SIMD the other wave covers the LDS latency, and the registers are needed
-        if (cc % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        for (int cc = 0; cc < NC; ++cc) {
+          const int cb = cc & 1;
+          if (cc + 1 < NC) {
+            opq[cb ^ 1] = lds_read_b128(qa + 16 * (cc + 1));
+            opo[cb ^ 1] = lds_read_b128(oa + 16 * (cc + 1));
+            opv[cb ^ 1] = lds_read_b128(vp + 16 * (cc + 1));
+          }
+          s = mfma32(opq[cb], kop[cc], s);
+          dp = mfma32(opo[cb], opv[cb], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
+      } else {  // the position bias needs the registers of the read-ahead buffers
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          s = mfma32(lds_read_b128(qa + 16 * cc), kop[cc], s);
+          dp = mfma32(lds_read_b128(oa + 16 * cc), lds_read_b128(vp + 16 * cc), dp);
+          if (cc % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_setprio(0);
       }
-      __builtin_amdgcn_s_setprio(0);
       // P = exp2(S c + bias - LSE log2 e), masked entries 0; dS = P (dP - D).  The position
       // bias: see alibi_addend (here the lane is the key).
       float pv[16];
@@ -576,6 +598,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
           pv[r] = ok ? pv[r] : 0.f;
         }
       }
+      // A operands of the dV / dK products (rows of the transposed dO and Q tiles), head-dim
+      // tile dt into one of two named buffers.  Tile 0 is read here, so its latency hides
+      // behind the elementwise work below; tile dt + 1 while tile dt's products issue.
+      bf16x8 ao[2][2], aq[2][2];
+      auto ld_dt = [&](int dt, bf16x8 (&o2)[2], bf16x8 (&q2)[2]) {
+        const bf16_t* ot = sOT + (32 * dt + l32) * TSTR + 8 * hh;
+        const bf16_t* qt = sQT + (32 * dt + l32) * TSTR + 8 * hh;
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          o2[c2] = lds_read_b128(ot + 16 * c2);
+          q2[c2] = lds_read_b128(qt + 16 * c2);
+        }
+      };
+      ld_dt(0, ao[0], aq[0]);
       bf16x8 pP[2], pS[2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
@@ -596,16 +632,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
         pS[c2][i0 + 2] = d23[0];
         pS[c2][i0 + 3] = d23[1];
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (A operands from the transposed tiles).
+      // dV^T += dO^T P and dK^T += Q^T dS.
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
-        const bf16_t* ot = sOT + (32 * dt + l32) * TSTR + 8 * hh;
-        const bf16_t* qt = sQT + (32 * dt + l32) * TSTR + 8 * hh;
+        const int cb = dt & 1;
+        if (dt + 1 < ND) ld_dt(dt + 1, ao[cb ^ 1], aq[cb ^ 1]);
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2) {
-          dv[dt] = mfma32(lds_read_b128(ot + 16 * c2), pP[c2], dv[dt]);
-          dk[dt] = mfma32(lds_read_b128(qt + 16 * c2), pS[c2], dk[dt]);
+          dv[dt] = mfma32(ao[cb][c2], pP[c2], dv[dt]);
+          dk[dt] = mfma32(aq[cb][c2], pS[c2], dk[dt]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
