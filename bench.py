@@ -321,7 +321,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default=None, help="workload name (default: headline)")
+    ap.add_argument("--workload", default=None, help="workload name (default: bf16_b2_h32_n8192_d128_causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the products-only MFMA throughput probe (profiling runs)")
@@ -330,8 +330,9 @@ def main() -> int:
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                          "(the hot path shards over (batch, head) pairs, see DESIGN.md)"}))
+        print(json.dumps({"error": "one GPU only: --gpus must be 1 (the attention kernels "
+                          "shard over (batch, head) pairs with no communication; a "
+                          "multi-GPU launch is not part of this benchmark)"}))
         return 2
 
     from exact_io_aware_fa2_amd.workloads import DECODE_WORKLOADS
@@ -340,12 +341,12 @@ def main() -> int:
 
     import torch
     from exact_io_aware_fa2_amd import fa
-    from exact_io_aware_fa2_amd.workloads import (ALIBI_WORKLOADS, FP8_WORKLOADS, HEADLINE,
+    from exact_io_aware_fa2_amd.workloads import (ALIBI_WORKLOADS, FP8_WORKLOADS, DEFAULT_WORKLOAD,
                                                   VARLEN_WORKLOADS, WORKLOADS, alibi_slopes,
                                                   make_fp8_inputs, make_inputs,
                                                   make_varlen_inputs)
 
-    name = args.workload or HEADLINE
+    name = args.workload or DEFAULT_WORKLOAD
     packed = name in VARLEN_WORKLOADS
     fp8 = name in FP8_WORKLOADS
     w = (VARLEN_WORKLOADS[name] if packed else FP8_WORKLOADS[name] if fp8 else

@@ -66,7 +66,7 @@ WORKLOADS = {
         window=4096, seed=1005),
 }
 
-HEADLINE = "bf16_b2_h32_n8192_d128_causal"
+DEFAULT_WORKLOAD = "bf16_b2_h32_n8192_d128_causal"
 
 def alibi_slopes(h: int) -> list:
     """The geometric slope set of the ALiBi method: head i (1-based) of h gets 2^(-8 i / h)."""
@@ -180,8 +180,8 @@ def length_mix(total: int, lo: int, hi: int, seed: int) -> tuple:
     return tuple(out)
 
 
-# A packed batch with the headline's token count (2 x 8192 rows of 32 heads, d=128,
-# causal), made of documents of 128 .. 8192 rows.
+# A packed batch with the token count of bf16_b2_h32_n8192_d128_causal (2 x 8192 rows of
+# 32 heads, d=128, causal), made of documents of 128 .. 8192 rows.
 VARLEN_WORKLOADS = {
     "bf16_varlen_t16384_h32_d128_causal": VarlenWorkload(
         "bf16_varlen_t16384_h32_d128_causal", length_mix(16384, 128, 8192, 2001), 32, 32, 128,

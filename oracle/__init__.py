@@ -7,7 +7,7 @@ the Python binding, and it never touches a GPU.
 
 Every function is the plain textbook definition written out in NumPy float64:
 full-row softmax over the allowed key set, no tiling over keys and no online
-rescaling.  Sources (the pages this build follows):
+rescaling.  Sources (the pages this oracle follows):
 
 * ainews.cool, "flash-attention transformer optimization", section 技术深度解析
   (technical deep dive): the attention formula Softmax(QK^T/sqrt(d))V, the N x N

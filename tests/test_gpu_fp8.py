@@ -2,7 +2,7 @@
 
 The oracle is the exact attention of the dequantised inputs.  The kernel's 8-bit products
 sum with less than float32 precision and it rounds its probability weights to E4M3 before
-the second product, so random inputs are judged by the per-row bounds derived in
+the second product, so random inputs are checked against the per-row bounds derived in
 tests/_parity.py (fp8_score_error, fp8_o_bound, check_fp8_lse).
 Inputs whose scores are small integers with a unit log2 scale make every weight an exact
 power of two: there the rounding is exact and O must meet the bf16 tolerances too, which
