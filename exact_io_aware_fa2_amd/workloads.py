@@ -73,14 +73,14 @@ def alibi_slopes(h: int) -> list:
     return [2.0 ** (-8.0 * i / h) for i in range(1, h + 1)]
 
 
-# The bench workload with the ALiBi position bias (the geometric slopes above).
+# bf16_b2_h32_n8192_d128_causal with the ALiBi position bias (the geometric slopes above).
 ALIBI_WORKLOADS = {
     "bf16_b2_h32_n8192_d128_causal_alibi": Workload(
         "bf16_b2_h32_n8192_d128_causal_alibi", "bf16", 2, 32, 32, 8192, 128, True, seed=1007,
         alibi=True),
 }
 
-# The bench workload's shape with 8-bit E4M3 inputs (forward only).
+# The shape of bf16_b2_h32_n8192_d128_causal with 8-bit E4M3 inputs (forward only).
 FP8_WORKLOADS = {
     "fp8_b2_h32_n8192_d128_causal": Workload("fp8_b2_h32_n8192_d128_causal", "fp8", 2, 32, 32,
                                              8192, 128, True, backward=False, seed=1006),
