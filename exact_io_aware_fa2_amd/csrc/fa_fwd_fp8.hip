@@ -217,19 +217,36 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 1) void fwd_fp8_kernel(
                         (window <= 0 || n0 + BN - 1 >= wr0 - window + 1);
     if (active) {
       // S^T pieces: keys n0 + 32 pc + [0, 32) x this wave's 32 rows.
+      // Up to d = 128 every K operand of the tile is read before its products and the
+      // V^T operands right after them, so LDS latency hides behind the products and the
+      // softmax; at d = 256 those registers would spill, and each piece reads its own.
+      constexpr bool kAhead = D <= 128;
       f32x16 sp[2];
+      i32x8 kop[kAhead ? 2 : 1][NCQ];
+      i32x8 vop[kAhead ? ND : 1];
+      auto read_k = [&](int pc, i32x8 (&dst)[NCQ]) {
+        const uint8_t* kp = sK + (32 * pc + l32) * KSTR + 32 * hh;
+#pragma unroll
+        for (int cc = 0; cc < NCQ; ++cc) dst[cc] = lds_read_32(kp + 64 * cc);
+      };
+      const uint8_t* vp = sV + l32 * VSTR + 32 * hh;
+      if constexpr (kAhead) {
+        read_k(0, kop[0]);
+        read_k(1, kop[1]);
+      }
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int pc = 0; pc < 2; ++pc) {
-        const uint8_t* kp = sK + (32 * pc + l32) * KSTR + 32 * hh;
-        i32x8 kop[NCQ];
-#pragma unroll
-        for (int cc = 0; cc < NCQ; ++cc) kop[cc] = lds_read_32(kp + 64 * cc);
+        if constexpr (!kAhead) read_k(pc, kop[0]);
         f32x16 s = zero16();
-        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int cc = 0; cc < NCQ; ++cc) s = mfma_f8(kop[cc], qop[cc], s);
-        __builtin_amdgcn_s_setprio(0);
+        for (int cc = 0; cc < NCQ; ++cc) s = mfma_f8(kop[kAhead ? pc : 0][cc], qop[cc], s);
         sp[pc] = s;
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if constexpr (kAhead) {
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt) vop[dt] = lds_read_32(vp + 32 * dt * VSTR);
       }
       float s[32];
 #pragma unroll
@@ -290,11 +307,10 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 1) void fwd_fp8_kernel(
         pk[g] = wd;
       }
       // O^T += V^T P^T over the whole 64-key tile.
-      const uint8_t* vp = sV + l32 * VSTR + 32 * hh;
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
-        acc[dt] = mfma_f8(lds_read_32(vp + 32 * dt * VSTR), pk, acc[dt]);
+        acc[dt] = mfma_f8(kAhead ? vop[dt] : lds_read_32(vp + 32 * dt * VSTR), pk, acc[dt]);
       __builtin_amdgcn_s_setprio(0);
     }
     if (nb + 1 < nb_hi) {
