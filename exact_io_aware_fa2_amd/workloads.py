@@ -282,3 +282,17 @@ def make_decode_inputs(w: DecodeWorkload, device: str | torch.device = "cpu"):
     v = draw((w.B, w.Nk, w.Hkv, w.d))
     lens = None if w.lengths is None else torch.tensor(w.lens, dtype=torch.int32).to(device)
     return q, k, v, lens
+
+
+# ------------------------------------------------------------------ tensors near the size limit
+# The entry points accept tensors of fewer than 2^31 elements (the kernels' row and buffer
+# arithmetic is 32-bit); the largest such tensors are drawn on the device itself, where a
+# host draw and copy of several GiB would dominate a test.
+MAX_ELEMS = 1 << 31
+
+
+def device_normal(shape, seed: int, device, dtype=torch.bfloat16):
+    """Seeded N(0, 1) draws made on `device` by torch's generator for that device, in dtype."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=dtype)

@@ -44,6 +44,8 @@ BAD_FWD = [
     (dict(d=96), fa.FA_ERR_UNSUPPORTED),
     (dict(d=512), fa.FA_ERR_UNSUPPORTED),
     (dict(B=1 << 12, N=1 << 12, Hq=1 << 4, Hkv=1 << 4, d=128), fa.FA_ERR_INVALID_ARG),
+    # exactly 2^31 elements: one row more than the largest accepted size
+    (dict(B=2, N=1 << 20, Hq=8, Hkv=2, d=128), fa.FA_ERR_INVALID_ARG),
 ]
 
 
