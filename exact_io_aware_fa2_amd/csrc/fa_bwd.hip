@@ -439,8 +439,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   const int qb_hi = (row_end + BQ - 1) / BQ;
   const int nq = max(0, qb_hi - qb_lo);
   const int total_it = G * nq;
-  // ALiBi slope (log2 units) of the query head of step it
-  auto slope_of = [&](int it) { return AL != 0 ? slopes[hkv * G + it / nq] * kLog2e : 0.f; };
+  // A step is (query head g of the group, query block qb_lo + qi), g-major.  Steps advance
+  // by counting, not by dividing the step index by nq (a scalar division per use).
+  struct Step {
+    int g, qi;
+  };
+  auto adv = [&](Step st) { return st.qi + 1 == nq ? Step{st.g + 1, 0} : Step{st.g, st.qi + 1}; };
+  // ALiBi slope (log2 units) of query head g of the group
+  auto slope_of = [&](int g) { return AL != 0 ? slopes[hkv * G + g] * kLog2e : 0.f; };
 
   f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -467,9 +473,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   // merge or feed arithmetic right away, or the wait for it lands right behind its issue.
   uint4 xr[2];
   float lraw = 0.f, draw = 0.f;
-  auto step_r0 = [&](int it) { return (qb_lo + it % nq) * BQ; };
-  auto gload = [&](int it) {
-    const int g = it / nq, hq = hkv * G + g, r0 = step_r0(it);
+  auto gload = [&](Step st) {
+    const int hq = hkv * G + st.g, r0 = (qb_lo + st.qi) * BQ;
     if (stager) {
       const bf16_t* base = (iso ? dO : Q) + ((size_t)seq0 * Hq + hq) * D + (size_t)r0 * qs;
       const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     draw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                         make_rsrc(Dv + l0, lbytes), (int)loff, 0, 0));
   };
-  auto swrite = [&](int buf, int it) {
+  auto swrite = [&](int buf, Step st) {
     bf16_t* sQ = reinterpret_cast<bf16_t*>(stage + buf * Cfg::BUFB);
     bf16_t* sO = sQ + Cfg::SQ;
     bf16_t* sQT = sO + Cfg::SQ;
@@ -506,18 +511,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       }
     }
     if (tid < BQ) {
-      const bool in = step_r0(it) + tid < N;
+      const bool in = (qb_lo + st.qi) * BQ + tid < N;
       // +inf -> P = 0 on padding rows.  Causal position bias: LSE + slope2 (row - r0) is
       // staged and slope2 (key - r0) added per lane, both small near the diagonal.
-      sL[tid] = in ? lraw * kLog2e + (AL == 1 ? slope_of(it) * tid : 0.f) : INFINITY;
+      sL[tid] = in ? lraw * kLog2e + (AL == 1 ? slope_of(st.g) * tid : 0.f) : INFINITY;
       sL[BQ + tid] = in ? draw : 0.f;
     }
   };
 
+  Step cur{0, 0};
+  Step nxt = adv(cur), far = adv(nxt);  // steps it, it + 1, it + 2
   if (total_it > 0) {
-    gload(0);
-    swrite(0, 0);
-    if (total_it > 1) gload(1);
+    gload(cur);
+    swrite(0, cur);
+    if (total_it > 1) gload(nxt);
   }
   __syncthreads();
   const bf16_t* vp = sV + (32 * w + l32) * STR + 8 * hh;  // V^T B operand rows of this wave
@@ -529,9 +536,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     const bf16_t* sOT = sQT + Cfg::SQT;
     const float* sL = reinterpret_cast<const float*>(sOT + Cfg::SQT);
     const float* sD = sL + BQ;
-    const int g = it / nq, qb = qb_lo + (it - g * nq);
-    const int r0 = qb * BQ;
-    (void)g;
+    const int r0 = (qb_lo + cur.qi) * BQ;
     const bool active = kw0 < N && (!causal || r0 + BQ - 1 >= kw0) &&
                         (window <= 0 || r0 <= kw0 + 31 + window - 1);
     if (active) {
@@ -574,7 +579,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       // P = exp2(S c + bias - LSE log2 e), masked entries 0; dS = P (dP - D).  The position
       // bias: see alibi_addend (here the lane is the key).
       float pv[16];
-      const float sl2 = slope_of(it);
+      const float sl2 = slope_of(cur.g);
       const float kstep = sl2 * (float)(key - r0);
       const float rbase = (float)(r0 + 4 * hh - key);
 #pragma unroll
@@ -648,10 +653,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       __builtin_amdgcn_s_setprio(0);
     }
     if (it + 1 < total_it) {
-      swrite(buf ^ 1, it + 1);
-      if (it + 2 < total_it) gload(it + 2);
+      swrite(buf ^ 1, nxt);
+      if (it + 2 < total_it) gload(far);
     }
     __syncthreads();
+    cur = nxt;
+    nxt = far;
+    far = adv(far);
   }
 
   if (key < N) {
