@@ -515,7 +515,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       // +inf -> P = 0 on padding rows.  Causal position bias: LSE + slope2 (row - r0) is
       // staged and slope2 (key - r0) added per lane, both small near the diagonal.
       sL[tid] = in ? lraw * kLog2e + (AL == 1 ? slope_of(st.g) * tid : 0.f) : INFINITY;
-      sL[BQ + tid] = in ? draw : 0.f;
+      sL[BQ + tid] = in ? -draw : 0.f;  // -D: the dP accumulator starts from it
     }
   };
 
@@ -546,7 +546,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       // The operands of k-step cc + 1 are read while k-step cc's products issue (two named
       // buffers); the scheduling barrier after each k-step keeps later reads from being
       // hoisted further, which would need more registers than two waves per SIMD leave.
-      f32x16 s = zero16(), dp = zero16();
+      // dP - D comes straight out of the products: the accumulator starts at -D of its rows.
+      f32x16 s = zero16(), dp;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 nd4 = *reinterpret_cast<const f32x4*>(sD + 8 * g4 + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * g4 + e] = nd4[e];
+      }
       if constexpr (AL == 0) {
         bf16x8 opq[2], opo[2], opv[2];
         opq[0] = lds_read_b128(qa);
@@ -620,10 +627,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       bf16x8 pP[2], pS[2];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 D4 = *reinterpret_cast<const f32x4*>(sD + 8 * g4 + 4 * hh);
         float dsv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dsv[e] = pv[4 * g4 + e] * (dp[4 * g4 + e] - D4[e]);
+        for (int e = 0; e < 4; ++e) dsv[e] = pv[4 * g4 + e] * dp[4 * g4 + e];
         const int c2 = g4 >> 1, i0 = 4 * (g4 & 1);
         const bf16x2 p01 = to_bf16x2(pv[4 * g4], pv[4 * g4 + 1]);
         const bf16x2 p23 = to_bf16x2(pv[4 * g4 + 2], pv[4 * g4 + 3]);
