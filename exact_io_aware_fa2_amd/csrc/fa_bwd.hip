@@ -222,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       // causal position bias: LSE + slope2 (row - r0) is staged, slope2 (key - r0) added per
       // lane (both small near the diagonal, where the weights are not negligible)
       sL[tid] = AL == 1 ? lreg + slope_of(buf_it) * tid : lreg;
-      sL[BQ + tid] = dreg;
+      sL[BQ + tid] = -dreg;  // -D: the dP accumulators start from it
     }
   };
 
@@ -259,7 +259,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           oa_op[cc] = lds_read_b128(oa + 16 * cc);
         }
         s[mt] = zero16();
-        dp[mt] = zero16();
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {  // dP - D straight out of the products
+          const f32x4 nd4 = *reinterpret_cast<const f32x4*>(sD + 32 * mt + 8 * g4 + 4 * hh);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[mt][4 * g4 + e] = nd4[e];
+        }
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
           s[mt] = mfma32(qa_op[cc], kop[cc], s[mt]);
@@ -305,10 +310,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 D4 = *reinterpret_cast<const f32x4*>(sD + 32 * mt + 8 * g4 + 4 * hh);
           float dsv[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dsv[e] = s[mt][4 * g4 + e] * (dp[mt][4 * g4 + e] - D4[e]);
+          for (int e = 0; e < 4; ++e) dsv[e] = s[mt][4 * g4 + e] * dp[mt][4 * g4 + e];
           const int c2 = g4 >> 1, i0 = 4 * (g4 & 1);
           const bf16x2 p01 = to_bf16x2(s[mt][4 * g4], s[mt][4 * g4 + 1]);
           const bf16x2 p23 = to_bf16x2(s[mt][4 * g4 + 2], s[mt][4 * g4 + 3]);
