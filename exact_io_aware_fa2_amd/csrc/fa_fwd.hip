@@ -331,7 +331,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
           rse = tree_sum(e);
         }
         bf16x8 pp[2];
-        float rs2[2] = {0.f, 0.f};  // two dot chains, one per half of the piece
+        float rs2[2] = {l_i, 0.f};  // two dot chains, one per half of the piece
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const bf16x2 pe = to_bf16x2(e[r], e[r + 1]);
@@ -339,8 +339,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
           pp[r >> 3][r & 7] = pe[0];
           pp[r >> 3][(r & 7) + 1] = pe[1];
         }
-        const float rs = rs2[0] + rs2[1];
-        l_i += rs;
+        l_i = rs2[0] + rs2[1];
         le_i += rse;
 
         // O^T += V^T P^T.
