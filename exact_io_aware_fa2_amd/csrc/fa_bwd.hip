@@ -290,8 +290,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           }
         }
       }
-      const bool need_mask = (kw0 + 32 > N) || (causal && kw0 + 31 > r0) ||
-                             (window > 0 && kw0 < r0 + BQ - window);
+      const bool need_mask = (kw0 + 32 > N) | ((causal != 0) & (kw0 + 31 > r0)) |
+                             ((window > 0) & (kw0 < r0 + BQ - window));
       if (need_mask) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
@@ -603,8 +603,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
           pv[4 * g4 + e] = fast_exp2(fmaf(s[4 * g4 + e], c, xr));
         }
       }
-      const bool need_mask = (kw0 + 32 > N) || (causal && kw0 + 31 > r0) ||
-                             (window > 0 && kw0 < r0 + BQ - window);
+      const bool need_mask = (kw0 + 32 > N) | ((causal != 0) & (kw0 + 31 > r0)) |
+                             ((window > 0) & (kw0 < r0 + BQ - window));
       if (need_mask) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -913,8 +913,8 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
             p[r] = fast_exp2(fmaf(s[r], c, alibi_addend<AL>(slope2, dbase,
                                                             (float)(8 * (r >> 2) + (r & 3)), lse2)));
         }
-        const bool need_mask = (k0 + 32 > N) || (causal && k0 + 31 > wr0) ||
-                               (window > 0 && k0 < wr0 + 32 - window);
+        const bool need_mask = (k0 + 32 > N) | ((causal != 0) & (k0 + 31 > wr0)) |
+                               ((window > 0) & (k0 < wr0 + 32 - window));
         if (need_mask) {
           const int kb0 = k0 + hh * 4;
 #pragma unroll

@@ -269,8 +269,9 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
         // sequence) the masked scores are first replaced by -inf under a wave-uniform branch;
         // exp2 of -inf is 0, so the max and exp loops below carry no per-element mask.  The
         // accumulator rescale sits in one wave-uniform block, so no branch copies it.
-        const bool need_mask = (k0 + 32 > N) || (causal && k0 + 31 > wr0) ||
-                               (window > 0 && k0 < wr0 + 32 - window);
+        // (bitwise, not short-circuit: a branch-free scalar condition)
+        const bool need_mask = (k0 + 32 > N) | ((causal != 0) & (k0 + 31 > wr0)) |
+                               ((window > 0) & (k0 < wr0 + 32 - window));
         if (need_mask) {
           const int kb0 = k0 + hh * 4;  // key of element r: kb0 + (r / 4) * 8 + r % 4
 #pragma unroll

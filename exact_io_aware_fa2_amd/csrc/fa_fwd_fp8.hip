@@ -255,8 +255,8 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 1) void fwd_fp8_kernel(
         s[16 + r] = sp[1][r];
       }
       // Masks (wave-uniform branch; masked scores become -inf, weight 0).
-      const bool need_mask = (n0 + BN > N) || (causal && n0 + BN - 1 > wr0) ||
-                             (window > 0 && n0 < wr0 + 32 - window);
+      const bool need_mask = (n0 + BN > N) | ((causal != 0) & (n0 + BN - 1 > wr0)) |
+                             ((window > 0) & (n0 < wr0 + 32 - window));
       if (need_mask) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
