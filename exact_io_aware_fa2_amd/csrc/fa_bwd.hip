@@ -913,8 +913,13 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
             p[r] = fast_exp2(fmaf(s[r], c, alibi_addend<AL>(slope2, dbase,
                                                             (float)(8 * (r >> 2) + (r & 3)), lse2)));
         }
-        const bool need_mask = (k0 + 32 > N) | ((causal != 0) & (k0 + 31 > wr0)) |
-                               ((window > 0) & (k0 < wr0 + 32 - window));
+        // Bitwise (branch-free) without a position bias; with one, the short-circuit form,
+        // which here leaves the register allocation without spills.
+        const bool need_mask =
+            AL == 0 ? (k0 + 32 > N) | ((causal != 0) & (k0 + 31 > wr0)) |
+                          ((window > 0) & (k0 < wr0 + 32 - window))
+                    : (k0 + 32 > N) || (causal && k0 + 31 > wr0) ||
+                          (window > 0 && k0 < wr0 + 32 - window);
         if (need_mask) {
           const int kb0 = k0 + hh * 4;
 #pragma unroll
