@@ -978,20 +978,18 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   using K8 = KV8Cfg<D <= 128 ? D : 128>;
   using QC = QCfg<D>;
   constexpr bool kWide = D <= 128;  // 8-wave key-block kernel
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = kWide ? hipFuncSetAttribute((const void*)bwd_dkdv8_kernel<D <= 128 ? D : 128, AL>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               K8::LDS_BYTES)
-                         : hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, AL>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               KC::LDS_BYTES);
+  // Dynamic LDS limits, set once (a function-local static: the first call is thread-safe).
+  static const hipError_t attr = [] {
+    const hipError_t e =
+        kWide ? hipFuncSetAttribute((const void*)bwd_dkdv8_kernel<D <= 128 ? D : 128, AL>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, K8::LDS_BYTES)
+              : hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, AL>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, KC::LDS_BYTES);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void*)bwd_dq_kernel<D, AL>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, QC::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+    return hipFuncSetAttribute((const void*)bwd_dq_kernel<D, AL>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, QC::LDS_BYTES);
+  }();
+  if (attr != hipSuccess) return attr;
   const long rows = a.cu ? (long)a.ntot * a.Hq : (long)a.B * a.N * a.Hq;
   constexpr int RPB = 256 / (D / 8);
   hipLaunchKernelGGL(bwd_pre_kernel<D>, dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,

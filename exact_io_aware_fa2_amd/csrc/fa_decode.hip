@@ -322,14 +322,11 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(const float* __restri
 template <int D>
 static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
   using Cfg = DecCfg<D>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       Cfg::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  // Dynamic LDS limit, set once (a function-local static: the first call is thread-safe).
+  static const hipError_t attr = hipFuncSetAttribute((const void*)decode_kernel<D>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
   const int nrg = (a.Hq / a.Hkv * a.Nq + 31) / 32;
   if (a.ev_start) {
     const hipError_t e = hipEventRecord(a.ev_start, st);

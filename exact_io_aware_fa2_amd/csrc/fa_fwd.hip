@@ -482,14 +482,11 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(
 template <int D, int AL>
 static hipError_t launch_fwd_bf16_d(const FwdArgs& a, hipStream_t st) {
   using Cfg = FwdCfg<D>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D, AL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       Cfg::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  // Dynamic LDS limit, set once (a function-local static: the first call is thread-safe).
+  static const hipError_t attr = hipFuncSetAttribute((const void*)fwd_bf16_kernel<D, AL>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
   const int num_m = (a.N + Cfg::BM - 1) / Cfg::BM;
   const int grid = a.B * a.Hq * num_m;
   hipLaunchKernelGGL((fwd_bf16_kernel<D, AL>), dim3(grid), dim3(Cfg::NT), Cfg::LDS_BYTES, st,
@@ -517,14 +514,11 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
 template <int D>
 static hipError_t launch_fwd_fp32_d(const FwdArgs& a, hipStream_t st) {
   using Cfg = Fp32Cfg<D>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)fwd_fp32_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       Cfg::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  // Dynamic LDS limit, set once (a function-local static: the first call is thread-safe).
+  static const hipError_t attr = hipFuncSetAttribute((const void*)fwd_fp32_kernel<D>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
   const int num_m = (a.N + Cfg::BM - 1) / Cfg::BM;
   const int grid = a.B * a.Hq * num_m;
   hipLaunchKernelGGL(fwd_fp32_kernel<D>, dim3(grid), dim3(256), Cfg::LDS_BYTES, st,

@@ -345,14 +345,11 @@ __global__ __launch_bounds__(Fp8Cfg<D>::NT, 1) void fwd_fp8_kernel(
 template <int D>
 static hipError_t launch_fwd_fp8_d(const FwdArgs& a, hipStream_t st) {
   using Cfg = Fp8Cfg<D>;
-  static bool attr_done = false;
-  if (!attr_done) {
-    hipError_t e = hipFuncSetAttribute((const void*)fwd_fp8_kernel<D>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       Cfg::LDS_BYTES);
-    if (e != hipSuccess) return e;
-    attr_done = true;
-  }
+  // Dynamic LDS limit, set once (a function-local static: the first call is thread-safe).
+  static const hipError_t attr = hipFuncSetAttribute((const void*)fwd_fp8_kernel<D>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
   const int num_m = (a.N + Cfg::BM - 1) / Cfg::BM;
   hipLaunchKernelGGL(fwd_fp8_kernel<D>, dim3(a.B * a.Hq * num_m), dim3(Cfg::NT), Cfg::LDS_BYTES,
                      st, (const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v,
