@@ -53,10 +53,11 @@ def fwd_flops(w) -> float:
 
 
 def _src_sha(name: str) -> str:
-    """Hash of a kernel source together with the device-code header every kernel includes."""
+    """Hash of a kernel source together with the device-code header every kernel includes and
+    the build script that holds the compiler flags."""
     h = hashlib.sha256()
-    for n in (name, "fa_common.hpp"):
-        with open(os.path.join(ROOT, "exact_io_aware_fa2_amd", "csrc", n), "rb") as f:
+    for rel in (os.path.join("csrc", name), os.path.join("csrc", "fa_common.hpp"), "build.py"):
+        with open(os.path.join(ROOT, "exact_io_aware_fa2_amd", rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 

@@ -8,10 +8,12 @@ there.  hipcc cross-compiles for gfx950 without a GPU present.
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -24,12 +26,19 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-munsafe-fp-atomics",
     # keep the compiler away from packed-fp32 VALU forms
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+
+# Per-source flags.  The two forward kernels measured 1-3 % faster (interleaved A/B runs)
+# with the backend's iterative register-minimising scheduler; the backward kernels are
+# fastest with the default one.
+FILE_FLAGS = {
+    "fa_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
+    "fa_fwd_fp8.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
+}
 
 
 def hipcc() -> str:
@@ -39,11 +48,7 @@ def hipcc() -> str:
     return cand
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile libfa.so; returns its path.  Raises on a compiler error."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + (extra_flags or []) + \
-        [os.path.join(CSRC, s) for s in SOURCES] + ["-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,6 +58,24 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{out}")
     if verbose and out.strip():
         print(out)
+
+
+def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+    """Compile every source to an object (in parallel) and link libfa.so; returns its path.
+    Raises on a compiler error."""
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="libfa_build_") as tmpdir:
+        jobs = []
+        for src in SOURCES:
+            obj = os.path.join(tmpdir, src.replace(".hip", ".o"))
+            jobs.append((obj, [cc] + HIPCC_FLAGS + FILE_FLAGS.get(src, []) + (extra_flags or []) +
+                         ["-c", os.path.join(CSRC, src), "-o", obj]))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), 8)) as pool:
+            for f in [pool.submit(_run, cmd, verbose) for _, cmd in jobs]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([cc, "--offload-arch=gfx950", "-shared", "-fPIC"] + [o for o, _ in jobs] +
+             ["-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 
