@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -66,6 +67,22 @@ fa_status launched(const char* fn, hipError_t e) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Tensors move through 16-byte vector loads and stores; the float32 row statistics and the
+// int32 / float32 side arrays through 4-byte ones.  (Null optional pointers pass.)
+bool misaligned(std::initializer_list<const void*> ptrs, uintptr_t bytes) {
+  for (const void* p : ptrs)
+    if (((uintptr_t)p & (bytes - 1)) != 0) return true;
+  return false;
+}
+fa_status check_align(const char* fn, std::initializer_list<const void*> t16,
+                      std::initializer_list<const void*> t4) {
+  if (misaligned(t16, 16) || misaligned(t4, 4))
+    return fail(FA_ERR_INVALID_ARG,
+                "%s: tensor pointers must be 16-byte aligned (row statistics and side arrays "
+                "4-byte aligned)", fn);
+  return FA_OK;
+}
+
 // Packed sequences: the shared checks on (Hq, Hkv, d, window, scale) run as for one batch
 // entry of `total` rows; on top, the offsets pointer, counts and grid size are checked.
 // The offsets themselves live on the device and are not read here (the kernels clamp
@@ -94,6 +111,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  const float* alibi_slopes, void* stream) {
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "fa_fwd: null pointer");
   fa_status st = check_common("fa_fwd", B, Hq, Hkv, N, d, causal, window, scale);
+  if (st == FA_OK) st = check_align("fa_fwd", {q, k, v, o}, {lse, alibi_slopes});
   if (st != FA_OK) return st;
   // The bf16 kernel works with the non-negative log2 scale |scale| log2(e) (a negative scale
   // negates Q exactly) and marks masked scores with -inf; for scale == 0 it gets a tiny
@@ -112,6 +130,7 @@ fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, 
   if (!q || !k || !v || !o || !lse)
     return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp32: null pointer");
   fa_status st = check_common("fa_fwd_fp32", B, Hq, Hkv, N, d, causal, window, scale);
+  if (st == FA_OK) st = check_align("fa_fwd_fp32", {q, k, v, o}, {lse});
   if (st != FA_OK) return st;
   fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal ? 1 : 0, window,
                 fabsf(scale) * fa::kHostLog2e, scale * fa::kHostLog2e, 0};
@@ -123,6 +142,7 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
                      int N, int d, int causal, int window, float scale, void* stream) {
   if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "fa_fwd_fp8: null pointer");
   fa_status st = check_common("fa_fwd_fp8", B, Hq, Hkv, N, d, causal, window, scale);
+  if (st == FA_OK) st = check_align("fa_fwd_fp8", {q, k, v, o}, {lse});
   if (st != FA_OK) return st;
   if (!(isfinite(descale_q) && descale_q > 0.f && isfinite(descale_k) && descale_k > 0.f &&
         isfinite(descale_v) && descale_v > 0.f))
@@ -154,6 +174,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
     return fail(FA_ERR_INVALID_ARG, "fa_bwd: null pointer");
   fa_status st = check_common("fa_bwd", B, Hq, Hkv, N, d, causal, window, scale);
+  if (st == FA_OK)
+    st = check_align("fa_bwd", {q, k, v, o, dO, dq, dk, dv}, {lse, alibi_slopes});
   if (st != FA_OK) return st;
   const size_t need = fa_bwd_workspace_size(B, Hq, Hkv, N, d, causal, window);
   if (!workspace || workspace_bytes < need)
@@ -185,6 +207,8 @@ fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, fl
     return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: null pointer");
   fa_status st = check_varlen("fa_fwd_varlen", cu_seqlens, num_seqs, total, max_seqlen, Hq,
                               Hkv, d, causal, window, scale);
+  if (st == FA_OK)
+    st = check_align("fa_fwd_varlen", {q, k, v, o}, {lse, cu_seqlens, alibi_slopes});
   if (st != FA_OK) return st;
   const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;  // as in fa_fwd
   fa::FwdArgs a{q, k, v, o, lse, num_seqs, Hq, Hkv, max_seqlen, d, causal ? 1 : 0, window,
@@ -209,6 +233,9 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
     return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: null pointer");
   fa_status st = check_varlen("fa_bwd_varlen", cu_seqlens, num_seqs, total, max_seqlen, Hq,
                               Hkv, d, causal, window, scale);
+  if (st == FA_OK)
+    st = check_align("fa_bwd_varlen", {q, k, v, o, dO, dq, dk, dv},
+                     {lse, cu_seqlens, alibi_slopes});
   if (st != FA_OK) return st;
   const size_t need = fa_bwd_varlen_workspace_size(total, Hq, Hkv, d);
   if (!workspace || workspace_bytes < need)
@@ -254,6 +281,7 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache,
     return fail(FA_ERR_INVALID_ARG, "fa_decode: null pointer");
   if (Nq <= 0) return fail(FA_ERR_INVALID_ARG, "fa_decode: Nq=%d must be positive", Nq);
   fa_status st = check_common("fa_decode", B, Hq, Hkv, Nk, d, causal, window, scale);
+  if (st == FA_OK) st = check_align("fa_decode", {q, k_cache, v_cache, o}, {lse, seqlens_k});
   if (st != FA_OK) return st;
   if (d != 64 && d != 128)
     return fail(FA_ERR_UNSUPPORTED, "fa_decode: head dim %d not supported (64 or 128)", d);

@@ -42,6 +42,9 @@
  *     nothing was enqueued and fa_last_error() describes the problem.
  *   - Stateless and re-entrant; the only state is the thread-local error message.
  *   - Output buffers must not alias input buffers.
+ *   - Tensor pointers (q, k, v, o, dO, dq, dk, dv, the caches) must be 16-byte aligned
+ *     and the float32 / int32 arrays (lse, cu_seqlens, seqlens_k, alibi_slopes) 4-byte
+ *     aligned, as any framework allocation is; FA_ERR_INVALID_ARG otherwise.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -54,8 +57,9 @@ extern "C" {
 
 typedef enum {
   FA_OK = 0,
-  FA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, Hq % Hkv != 0, window < 0,
-                             non-finite scale, size product overflowing 2^31 elements   */
+  FA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, non-positive size, Hq % Hkv != 0,
+                             window < 0, non-finite scale, size product overflowing 2^31
+                             elements                                                   */
   FA_ERR_UNSUPPORTED = 2, /* head dim outside {64, 128, 256}                             */
   FA_ERR_WORKSPACE = 3,   /* fa_bwd workspace missing or smaller than required           */
   FA_ERR_HIP = 4          /* the HIP runtime reported an error at launch                  */

@@ -216,3 +216,36 @@ def test_decode_validation_and_splits():
     st = fa.fa_decode(None, fake, fake, None, fake, fake, 1, 1, 1, 1, 8, 64, 1, 0, 0.1, 1, None,
                       0, stream=0)
     assert st == fa.FA_ERR_INVALID_ARG and "null" in fa.fa_last_error()
+
+
+# Alignment: tensor pointers 16 bytes, row statistics and side arrays 4 bytes.  Each call
+# passes one misaligned pointer (all others aligned fakes, never dereferenced).
+_A = 256
+
+
+def _misaligned_calls(t16, t4):
+    A = _A
+    return {
+        "fa_fwd": lambda: fa.fa_fwd(t16, A, A, A, t4, 1, 2, 2, 16, 64, 0, 0, 0.125, stream=0),
+        "fa_fwd_fp32": lambda: fa.fa_fwd_fp32(t16, A, A, A, t4, 1, 2, 2, 16, 64, 0, 0, 0.125,
+                                              stream=0),
+        "fa_fwd_fp8": lambda: fa.fa_fwd_fp8(A, t16, A, A, t4, 1.0, 1.0, 1.0, 1, 2, 2, 16, 64, 0,
+                                            0, 0.125, stream=0),
+        "fa_bwd": lambda: fa.fa_bwd(A, A, A, A, A, t4, A, A, t16, 1, 2, 2, 16, 64, 0, 0, 0.125,
+                                    A, 1 << 20, stream=0),
+        "fa_fwd_varlen": lambda: fa.fa_fwd_varlen(A, A, t16, A, t4, A, 1, 16, 16, 2, 2, 64, 0, 0,
+                                                  0.125, stream=0),
+        "fa_bwd_varlen": lambda: fa.fa_bwd_varlen(A, A, A, A, t16, t4, A, A, A, A, 1, 16, 16, 2,
+                                                  2, 64, 0, 0, 0.125, A, 1 << 20, stream=0),
+        "fa_decode": lambda: fa.fa_decode(A, A, t16, None, A, t4, 1, 2, 2, 1, 16, 64, 1, 0, 0.125,
+                                          1, None, 0, stream=0),
+    }
+
+
+@pytest.mark.parametrize("entry", sorted(_misaligned_calls(_A, _A)))
+@pytest.mark.parametrize("t16,t4", [(_A + 8, _A), (_A, _A + 2)], ids=["tensor+8", "stats+2"])
+def test_misaligned_pointers_are_rejected(entry, t16, t4):
+    st = _misaligned_calls(t16, t4)[entry]()
+    assert st == fa.FA_ERR_INVALID_ARG
+    assert "aligned" in fa.fa_last_error()
+
