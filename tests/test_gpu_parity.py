@@ -37,6 +37,8 @@ SHAPES = [
     (2, 4, 4, 1000, 128, True, 0),
     (1, 2, 2, 700, 256, True, 129),
     (1, 8, 8, 1024, 64, False, 0),
+    (1, 16, 2, 320, 64, True, 0),     # 8 query heads per KV head
+    (1, 16, 1, 200, 128, False, 50),  # one KV head for all 16 query heads
 ]
 
 
