@@ -751,7 +751,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   }
   const size_t li = stat_base(cu, ntot, b, Hq, hq, Nmax, seq0) + row;
   const float lse2 = row < N ? LSE[li] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
-  const float dval = row < N ? Dv[li] : 0.f;
+  const float ndval = row < N ? -Dv[li] : 0.f;  // -D of this lane's row
   const float slope2 = AL != 0 ? slopes[hq] * kLog2e : 0.f;
 
   int kv_lo = 0, kv_hi = N;
@@ -871,30 +871,39 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
         // S^T = K Q^T and dP^T = V dO^T: keys k0 + [0, 32) x this wave's rows.
         const bf16_t* kp = sK + (32 * kt + l32) * KSTR + 8 * hh;
         const bf16_t* vp = sV + (32 * kt + l32) * KSTR + 8 * hh;
-        // Operands are read ahead of their MFMAs when registers allow (d <= 128).
+        // d <= 128: the operands of k-step cc + 1 are read while k-step cc's products issue
+        // (two named buffers, a scheduling barrier per step), as in the key-block kernel.
+        // dP^T - D comes straight out of the products: the accumulator starts at -D.
         constexpr bool kAhead = D <= 128;
-        constexpr int NA = kAhead ? NC : 1;
-        bf16x8 ka[NA], va[NA];
+        f32x16 s = zero16(), dp;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = ndval;
         if constexpr (kAhead) {
+          bf16x8 ok[2], ov[2];
+          ok[0] = lds_read_b128(kp);
+          ov[0] = lds_read_b128(vp);
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int cc = 0; cc < NC; ++cc) {
-            ka[cc] = lds_read_b128(kp + 16 * cc);
-            va[cc] = lds_read_b128(vp + 16 * cc);
+            const int cb = cc & 1;
+            if (cc + 1 < NC) {
+              ok[cb ^ 1] = lds_read_b128(kp + 16 * (cc + 1));
+              ov[cb ^ 1] = lds_read_b128(vp + 16 * (cc + 1));
+            }
+            s = mfma32(ok[cb], qop[cc], s);
+            dp = mfma32(ov[cb], oop[cc], dp);
+            __builtin_amdgcn_sched_barrier(0);
           }
-        }
-        f32x16 s = zero16(), dp = zero16();
-        __builtin_amdgcn_s_setprio(1);
+          __builtin_amdgcn_s_setprio(0);
+        } else {
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          if constexpr (kAhead) {
-            s = mfma32(ka[cc], qop[cc], s);
-            dp = mfma32(va[cc], oop[cc], dp);
-          } else {
+          for (int cc = 0; cc < NC; ++cc) {
             s = mfma32(lds_read_b128(kp + 16 * cc), qop[cc], s);
             dp = mfma32(lds_read_b128(vp + 16 * cc), oop[cc], dp);
           }
+          __builtin_amdgcn_s_setprio(0);
         }
-        __builtin_amdgcn_s_setprio(0);
         const bf16_t* tp = sKT + l32 * TSTR + 8 * hh + 32 * kt;
         constexpr int NTA = kAhead ? ND : 1;
         bf16x8 ta[NTA][2];
@@ -931,7 +940,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
         bf16x8 pS[2];
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const bf16x2 d2 = to_bf16x2(p[r] * (dp[r] - dval), p[r + 1] * (dp[r + 1] - dval));
+          const bf16x2 d2 = to_bf16x2(p[r] * dp[r], p[r + 1] * dp[r + 1]);
           pS[r >> 3][r & 7] = d2[0];
           pS[r >> 3][(r & 7) + 1] = d2[1];
         }
