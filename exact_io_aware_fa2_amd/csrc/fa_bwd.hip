@@ -558,35 +558,24 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) dp[4 * g4 + e] = nd4[e];
       }
-      if constexpr (AL == 0) {
-        bf16x8 opq[2], opo[2], opv[2];
-        opq[0] = lds_read_b128(qa);
-        opo[0] = lds_read_b128(oa);
-        opv[0] = lds_read_b128(vp);
-        __builtin_amdgcn_s_setprio(1);
+      bf16x8 opq[2], opo[2], opv[2];
+      opq[0] = lds_read_b128(qa);
+      opo[0] = lds_read_b128(oa);
+      opv[0] = lds_read_b128(vp);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          const int cb = cc & 1;
-          if (cc + 1 < NC) {
-            opq[cb ^ 1] = lds_read_b128(qa + 16 * (cc + 1));
-            opo[cb ^ 1] = lds_read_b128(oa + 16 * (cc + 1));
-            opv[cb ^ 1] = lds_read_b128(vp + 16 * (cc + 1));
-          }
-          s = mfma32(opq[cb], kop[cc], s);
-          dp = mfma32(opo[cb], opv[cb], dp);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int cc = 0; cc < NC; ++cc) {
+        const int cb = cc & 1;
+        if (cc + 1 < NC) {
+          opq[cb ^ 1] = lds_read_b128(qa + 16 * (cc + 1));
+          opo[cb ^ 1] = lds_read_b128(oa + 16 * (cc + 1));
+          opv[cb ^ 1] = lds_read_b128(vp + 16 * (cc + 1));
         }
-        __builtin_amdgcn_s_setprio(0);
-      } else {  // the position bias needs the registers of the read-ahead buffers
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          s = mfma32(lds_read_b128(qa + 16 * cc), kop[cc], s);
-          dp = mfma32(lds_read_b128(oa + 16 * cc), lds_read_b128(vp + 16 * cc), dp);
-          if (cc % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-        }
-        __builtin_amdgcn_s_setprio(0);
+        s = mfma32(opq[cb], kop[cc], s);
+        dp = mfma32(opo[cb], opv[cb], dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       // P = exp2(S c + bias - LSE log2 e), masked entries 0; dS = P (dP - D).  The position
       // bias: see alibi_addend (here the lane is the key).
       float pv[16];
