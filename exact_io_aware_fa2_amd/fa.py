@@ -208,6 +208,21 @@ def _shapes(q, k, v):
     return B, N, Hq, k.shape[2], d
 
 
+def _expect(t, name, shape, dtype, device):
+    """A caller-supplied tensor must match what the kernels read or write: exact shape and
+    dtype, contiguous, on the inputs' device (a smaller buffer would be overrun)."""
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous()
+            or t.device != device):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}; got {tuple(t.shape)} {t.dtype} on {t.device}")
+    return t
+
+
+def _same_dtype_device(*ts):
+    if any(t.dtype != ts[0].dtype for t in ts) or any(t.device != ts[0].device for t in ts):
+        raise ValueError("q, k and v must share one dtype and one device")
+
+
 def _slopes(alibi_slopes, Hq):
     """Check an optional ALiBi slope tensor: float32, contiguous, on the device, Hq values."""
     if alibi_slopes is None:
@@ -224,11 +239,11 @@ def forward(q, k, v, causal=False, window=0, scale=None, out=None, lse=None, str
             alibi_slopes=None):
     """O, LSE = attention(q, k, v); bf16 or fp32 tensors in [B, N, H, d] layout."""
     B, N, Hq, Hkv, d = _shapes(q, k, v)
+    _same_dtype_device(q, k, v)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, N), device=q.device, dtype=torch.float32)
+    out = torch.empty_like(q) if out is None else _expect(out, "out", q.shape, q.dtype, q.device)
+    lse = (torch.empty((B, Hq, N), device=q.device, dtype=torch.float32) if lse is None
+           else _expect(lse, "lse", (B, Hq, N), torch.float32, q.device))
     if q.dtype == torch.bfloat16:
         _check(fa_fwd(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, stream,
                       _slopes(alibi_slopes, Hq)))
@@ -249,11 +264,13 @@ def forward_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, windo
         if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
             raise ValueError(f"E4M3 codes expected (uint8 or float8_e4m3fn), got {t.dtype}")
     B, N, Hq, Hkv, d = _shapes(q8, k8, v8)
+    if any(t.device != q8.device for t in (k8, v8)):
+        raise ValueError("q, k and v must be on one device")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    if out is None:
-        out = torch.empty((B, N, Hq, d), device=q8.device, dtype=torch.bfloat16)
-    if lse is None:
-        lse = torch.empty((B, Hq, N), device=q8.device, dtype=torch.float32)
+    out = (torch.empty((B, N, Hq, d), device=q8.device, dtype=torch.bfloat16) if out is None
+           else _expect(out, "out", (B, N, Hq, d), torch.bfloat16, q8.device))
+    lse = (torch.empty((B, Hq, N), device=q8.device, dtype=torch.float32) if lse is None
+           else _expect(lse, "lse", (B, Hq, N), torch.float32, q8.device))
     _check(fa_fwd_fp8(q8, k8, v8, out, lse, descale_q, descale_k, descale_v, B, Hq, Hkv, N, d,
                       causal, window, scale, stream))
     return out, lse
@@ -270,10 +287,17 @@ def backward(q, k, v, o, dO, lse, causal=False, window=0, scale=None, dq=None, d
              dv=None, workspace=None, stream=None, alibi_slopes=None):
     """dQ, dK, dV of L = sum(O * dO) for bf16 tensors."""
     B, N, Hq, Hkv, d = _shapes(q, k, v)
+    _same_dtype_device(q, k, v)
+    if q.dtype != torch.bfloat16:
+        raise ValueError(f"the backward takes bfloat16 tensors, got {q.dtype}")
+    dev = q.device
+    _expect(o, "o", q.shape, q.dtype, dev)
+    _expect(dO, "dO", q.shape, q.dtype, dev)
+    _expect(lse, "lse", (B, Hq, N), torch.float32, dev)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q) if dq is None else _expect(dq, "dq", q.shape, q.dtype, dev)
+    dk = torch.empty_like(k) if dk is None else _expect(dk, "dk", k.shape, k.dtype, dev)
+    dv = torch.empty_like(v) if dv is None else _expect(dv, "dv", v.shape, v.dtype, dev)
     if workspace is None:
         workspace = workspace_for(B, Hq, Hkv, N, d, causal, window, q.device)
     _check(fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
@@ -297,8 +321,11 @@ def _shapes_varlen(q, k, v, cu_seqlens):
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda:
         raise ValueError("cu_seqlens must be a 1-D int32 device tensor")
     for t in (q, k, v, cu_seqlens):
-        if not t.is_contiguous():
-            raise ValueError("tensors must be contiguous")
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("tensors must be contiguous and on one device")
+    for t in (q, k, v):
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"packed sequences take bfloat16 tensors, got {t.dtype}")
     return T, Hq, k.shape[1], d, cu_seqlens.numel() - 1
 
 
@@ -307,8 +334,9 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, scal
     """O [total, Hq, d], LSE [Hq, total] for packed bf16 sequences."""
     T, Hq, Hkv, d, S = _shapes_varlen(q, k, v, cu_seqlens)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((Hq, T), device=q.device, dtype=torch.float32) if lse is None else lse
+    out = torch.empty_like(q) if out is None else _expect(out, "out", q.shape, q.dtype, q.device)
+    lse = (torch.empty((Hq, T), device=q.device, dtype=torch.float32) if lse is None
+           else _expect(lse, "lse", (Hq, T), torch.float32, q.device))
     _check(fa_fwd_varlen(q, k, v, out, lse, cu_seqlens, S, T, max_seqlen, Hq, Hkv, d, causal,
                          window, scale, stream, _slopes(alibi_slopes, Hq)))
     return out, lse
@@ -326,10 +354,14 @@ def backward_varlen(q, k, v, o, dO, lse, cu_seqlens, max_seqlen, causal=False, w
                     alibi_slopes=None):
     """dQ, dK, dV of L = sum(O * dO) for packed bf16 sequences."""
     T, Hq, Hkv, d, S = _shapes_varlen(q, k, v, cu_seqlens)
+    dev = q.device
+    _expect(o, "o", q.shape, q.dtype, dev)
+    _expect(dO, "dO", q.shape, q.dtype, dev)
+    _expect(lse, "lse", (Hq, T), torch.float32, dev)
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    dq = torch.empty_like(q) if dq is None else _expect(dq, "dq", q.shape, q.dtype, dev)
+    dk = torch.empty_like(k) if dk is None else _expect(dk, "dk", k.shape, k.dtype, dev)
+    dv = torch.empty_like(v) if dv is None else _expect(dv, "dv", v.shape, v.dtype, dev)
     if workspace is None:
         workspace = workspace_for_varlen(T, Hq, Hkv, d, q.device)
     _check(fa_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, S, T, max_seqlen, Hq, Hkv,
@@ -356,8 +388,11 @@ def decode(q, k_cache, v_cache, seqlens_k=None, causal=True, window=0, scale=Non
                                   or not seqlens_k.is_cuda):
         raise ValueError("seqlens_k must be an int32 device tensor of B lengths")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32) if lse is None else lse
+    if any(t.device != q.device for t in (k_cache, v_cache)):
+        raise ValueError("q and the caches must be on one device")
+    out = torch.empty_like(q) if out is None else _expect(out, "out", q.shape, q.dtype, q.device)
+    lse = (torch.empty((B, Hq, Nq), device=q.device, dtype=torch.float32) if lse is None
+           else _expect(lse, "lse", (B, Hq, Nq), torch.float32, q.device))
     nbytes = fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)

@@ -249,3 +249,17 @@ def test_misaligned_pointers_are_rejected(entry, t16, t4):
     assert st == fa.FA_ERR_INVALID_ARG
     assert "aligned" in fa.fa_last_error()
 
+
+
+def test_python_buffer_checks():
+    import torch
+    t = torch.empty(2, 3, dtype=torch.float32)
+    assert fa._expect(t, "x", (2, 3), torch.float32, t.device) is t
+    with pytest.raises(ValueError, match="shape"):
+        fa._expect(t, "x", (3, 2), torch.float32, t.device)
+    with pytest.raises(ValueError):
+        fa._expect(t, "x", (2, 3), torch.bfloat16, t.device)
+    with pytest.raises(ValueError):
+        fa._expect(t.t(), "x", (3, 2), torch.float32, t.device)  # not contiguous
+    with pytest.raises(ValueError, match="one dtype"):
+        fa._same_dtype_device(t, t.to(torch.bfloat16))

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+from exact_io_aware_fa2_amd import fa
 from exact_io_aware_fa2_amd.workloads import make_inputs, small_case
 from tests._parity import (FP32_REL, check_grad, check_lse, check_o, gpu_bwd, gpu_fwd, rel_fro,
                            to64, workers)
@@ -198,3 +199,17 @@ def test_forward_is_deterministic_and_stream_ordered():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
     assert (dq1.float() - dq2.float()).abs().max().item() <= 1e-2
+
+
+def test_wrong_caller_buffers_are_rejected_before_launch():
+    w = _case((1, 2, 2, 64, 64, True, 0))
+    q, k, v, do = make_inputs(w, "cuda")
+    with pytest.raises(ValueError, match="out"):
+        fa.forward(q, k, v, causal=True, out=torch.empty(1, 32, 2, 64, dtype=q.dtype, device="cuda"))
+    o, lse = gpu_fwd(q, k, v, True, 0, w.scale)
+    with pytest.raises(ValueError, match="lse"):
+        fa.backward(q, k, v, o, do, lse[:, :1], causal=True)
+    with pytest.raises(ValueError, match="dq"):
+        fa.backward(q, k, v, o, do, lse, causal=True, dq=torch.empty_like(q, dtype=torch.float32))
+    with pytest.raises(ValueError, match="one dtype"):
+        fa.forward(q, k.float(), v, causal=True)
