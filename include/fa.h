@@ -61,7 +61,7 @@ typedef enum {
                              window < 0, non-finite scale, size product overflowing 2^31
                              elements                                                   */
   FA_ERR_UNSUPPORTED = 2, /* head dim outside {64, 128, 256}                             */
-  FA_ERR_WORKSPACE = 3,   /* fa_bwd workspace missing or smaller than required           */
+  FA_ERR_WORKSPACE = 3,   /* workspace missing, too small or not 256-byte aligned        */
   FA_ERR_HIP = 4          /* the HIP runtime reported an error at launch                  */
 } fa_status;
 
