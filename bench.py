@@ -402,8 +402,8 @@ def main() -> int:
             st = fa.fa_fwd_fp8(q, k, v, o, lse, *factors, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal,
                                w.window, w.scale, sh)
         elif slopes is not None:
-            st = fa.fa_fwd(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
-                           w.scale, sh, alibi_slopes=slopes)
+            st = fa.fa_fwd_alibi(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
+                                 w.scale, slopes, sh)
         else:
             st = fwd_fn(q, k, v, o, lse, w.B, w.Hq, w.Hkv, w.N, w.d, w.causal, w.window,
                         w.scale, sh)
@@ -414,9 +414,12 @@ def main() -> int:
         if packed:
             st = fa.fa_bwd_varlen(q, k, v, o, do, lse, dq, dk, dv, cu, S, T, M, w.Hq, w.Hkv,
                                   w.d, w.causal, w.window, w.scale, ws, ws_bytes, sh)
+        elif slopes is not None:
+            st = fa.fa_bwd_alibi(q, k, v, o, do, lse, dq, dk, dv, w.B, w.Hq, w.Hkv, w.N, w.d,
+                                 w.causal, w.window, w.scale, ws, ws_bytes, slopes, sh)
         else:
             st = fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, w.B, w.Hq, w.Hkv, w.N, w.d,
-                           w.causal, w.window, w.scale, ws, ws_bytes, sh, alibi_slopes=slopes)
+                           w.causal, w.window, w.scale, ws, ws_bytes, sh)
         if st != fa.FA_OK:
             raise RuntimeError(fa.fa_last_error())
 

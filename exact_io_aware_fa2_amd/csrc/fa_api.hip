@@ -40,6 +40,19 @@ fa_status ok() {
 constexpr int64_t kMaxElems = (int64_t)1 << 31;  // kernels index rows with 32-bit ints
 constexpr int kMaxSplits = 256;                  // key chunks per sequence in fa_decode
 
+// Product of non-negative factors, saturated at kMaxElems: never overflows, whatever int
+// sizes a caller passes (every partial product stays below 2^31 before the next factor).
+int64_t sat_mul(std::initializer_list<int64_t> xs) {
+  int64_t p = 1;
+  for (int64_t x : xs) {
+    if (x <= 0) return 0;
+    if (x >= kMaxElems || p >= kMaxElems / x + 1) return kMaxElems;
+    p *= x;
+    if (p >= kMaxElems) return kMaxElems;
+  }
+  return p;
+}
+
 fa_status check_common(const char* fn, int B, int Hq, int Hkv, int N, int d, int causal,
                        int window, float scale) {
   (void)causal;
@@ -52,10 +65,9 @@ fa_status check_common(const char* fn, int B, int Hq, int Hkv, int N, int d, int
   if (!isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "%s: scale must be finite", fn);
   if (d != 64 && d != 128 && d != 256)
     return fail(FA_ERR_UNSUPPORTED, "%s: head dim %d not supported (64, 128 or 256)", fn, d);
-  const int64_t rows = (int64_t)B * N * Hq;
-  if (rows * d >= kMaxElems || (int64_t)B * Hq * N >= kMaxElems)
-    return fail(FA_ERR_INVALID_ARG, "%s: B*N*Hq*d = %lld elements exceeds 2^31", fn,
-                (long long)(rows * d));
+  if (sat_mul({B, N, Hq, d}) >= kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "%s: B*N*Hq*d = %.4g elements reaches 2^31", fn,
+                (double)B * N * Hq * d);
   return FA_OK;
 }
 
@@ -97,8 +109,102 @@ fa_status check_varlen(const char* fn, const int* cu, int num_seqs, int total, i
     return fail(FA_ERR_INVALID_ARG, "%s: max_seqlen=%d exceeds total=%d", fn, max_seqlen, total);
   fa_status st = check_common(fn, 1, Hq, Hkv, total, d, causal, window, scale);
   if (st != FA_OK) return st;
-  if ((int64_t)num_seqs * Hq * ((max_seqlen + 31) / 32) >= kMaxElems)
+  if (sat_mul({num_seqs, Hq, (max_seqlen + 31) / 32}) >= kMaxElems)
     return fail(FA_ERR_INVALID_ARG, "%s: num_seqs * Hq * max_seqlen too large for one grid", fn);
+  return FA_OK;
+}
+
+// The bf16 forward behind fa_fwd and fa_fwd_alibi (slopes == nullptr: no position bias).
+fa_status fwd_bf16(const char* fn, const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int Hq, int Hkv, int N, int d, int causal, int window,
+                   float scale, const float* slopes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  fa_status st = check_common(fn, B, Hq, Hkv, N, d, causal, window, scale);
+  if (st == FA_OK) st = check_align(fn, {q, k, v, o}, {lse, slopes});
+  if (st != FA_OK) return st;
+  // The bf16 kernel works with the non-negative log2 scale |scale| log2(e) (a negative scale
+  // negates Q exactly) and marks masked scores with -inf; for scale == 0 it gets a tiny
+  // positive value instead of 0 so that -inf * scale stays -inf (every unmasked weight still
+  // rounds to exactly 1).
+  const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal ? 1 : 0, window, c2,
+                scale * fa::kHostLog2e, scale < 0.f ? 1 : 0};
+  a.slopes = slopes;
+  return launched(fn, fa::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+fa_status bwd_bf16(const char* fn, const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                   int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                   void* workspace, size_t workspace_bytes, const float* slopes,
+                   void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  fa_status st = check_common(fn, B, Hq, Hkv, N, d, causal, window, scale);
+  if (st == FA_OK) st = check_align(fn, {q, k, v, o, dO, dq, dk, dv}, {lse, slopes});
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_workspace_size(B, Hq, Hkv, N, d, causal, window);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, static_cast<float*>(workspace), B, Hq, Hkv,
+                N, d, causal ? 1 : 0, window, scale, scale * fa::kHostLog2e, g_time_start,
+                g_time_stop};
+  g_time_start = g_time_stop = nullptr;
+  a.slopes = slopes;
+  return launched(fn, fa::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+fa_status fwd_varlen(const char* fn, const void* q, const void* k, const void* v, void* o,
+                     float* lse, const int* cu_seqlens, int num_seqs, int total,
+                     int max_seqlen, int Hq, int Hkv, int d, int causal, int window,
+                     float scale, const float* slopes, void* stream) {
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  fa_status st = check_varlen(fn, cu_seqlens, num_seqs, total, max_seqlen, Hq, Hkv, d, causal,
+                              window, scale);
+  if (st == FA_OK) st = check_align(fn, {q, k, v, o}, {lse, cu_seqlens, slopes});
+  if (st != FA_OK) return st;
+  const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;  // as in fwd_bf16
+  fa::FwdArgs a{q, k, v, o, lse, num_seqs, Hq, Hkv, max_seqlen, d, causal ? 1 : 0, window,
+                c2, scale * fa::kHostLog2e, scale < 0.f ? 1 : 0, cu_seqlens, total};
+  a.slopes = slopes;
+  return launched(fn, fa::launch_fwd_bf16(a, (hipStream_t)stream));
+}
+
+fa_status bwd_varlen(const char* fn, const void* q, const void* k, const void* v,
+                     const void* o, const void* dO, const float* lse, void* dq, void* dk,
+                     void* dv, const int* cu_seqlens, int num_seqs, int total, int max_seqlen,
+                     int Hq, int Hkv, int d, int causal, int window, float scale,
+                     void* workspace, size_t workspace_bytes, const float* slopes,
+                     void* stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  fa_status st = check_varlen(fn, cu_seqlens, num_seqs, total, max_seqlen, Hq, Hkv, d, causal,
+                              window, scale);
+  if (st == FA_OK)
+    st = check_align(fn, {q, k, v, o, dO, dq, dk, dv}, {lse, cu_seqlens, slopes});
+  if (st != FA_OK) return st;
+  const size_t need = fa_bwd_varlen_workspace_size(total, Hq, Hkv, d);
+  if (!workspace || workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 255) != 0)
+    return fail(FA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, static_cast<float*>(workspace), num_seqs, Hq,
+                Hkv, max_seqlen, d, causal ? 1 : 0, window, scale, scale * fa::kHostLog2e,
+                g_time_start, g_time_stop, cu_seqlens, total};
+  g_time_start = g_time_stop = nullptr;
+  a.slopes = slopes;
+  return launched(fn, fa::launch_bwd_bf16(a, (hipStream_t)stream));
+}
+
+// The *_alibi entry points require their slope array.
+fa_status need_slopes(const char* fn, const float* slopes) {
+  if (!slopes)
+    return fail(FA_ERR_INVALID_ARG, "%s: null alibi_slopes (use the plain entry point for no "
+                "position bias)", fn);
   return FA_OK;
 }
 
@@ -108,20 +214,18 @@ extern "C" {
 
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int Hq, int Hkv, int N, int d, int causal, int window, float scale,
-                 const float* alibi_slopes, void* stream) {
-  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_INVALID_ARG, "fa_fwd: null pointer");
-  fa_status st = check_common("fa_fwd", B, Hq, Hkv, N, d, causal, window, scale);
-  if (st == FA_OK) st = check_align("fa_fwd", {q, k, v, o}, {lse, alibi_slopes});
+                 void* stream) {
+  return fwd_bf16("fa_fwd", q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, nullptr,
+                  stream);
+}
+
+fa_status fa_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                       const float* alibi_slopes, void* stream) {
+  const fa_status st = need_slopes("fa_fwd_alibi", alibi_slopes);
   if (st != FA_OK) return st;
-  // The bf16 kernel works with the non-negative log2 scale |scale| log2(e) (a negative scale
-  // negates Q exactly) and marks masked scores with -inf; for scale == 0 it gets a tiny
-  // positive value instead of 0 so that -inf * scale stays -inf (every unmasked weight still
-  // rounds to exactly 1).
-  const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;
-  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, d, causal ? 1 : 0, window, c2,
-                scale * fa::kHostLog2e, scale < 0.f ? 1 : 0};
-  a.slopes = alibi_slopes;
-  return launched("fa_fwd", fa::launch_fwd_bf16(a, (hipStream_t)stream));
+  return fwd_bf16("fa_fwd_alibi", q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale,
+                  alibi_slopes, stream);
 }
 
 fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -170,26 +274,20 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, i
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
                  int N, int d, int causal, int window, float scale, void* workspace,
-                 size_t workspace_bytes, const float* alibi_slopes, void* stream) {
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
-    return fail(FA_ERR_INVALID_ARG, "fa_bwd: null pointer");
-  fa_status st = check_common("fa_bwd", B, Hq, Hkv, N, d, causal, window, scale);
-  if (st == FA_OK)
-    st = check_align("fa_bwd", {q, k, v, o, dO, dq, dk, dv}, {lse, alibi_slopes});
+                 size_t workspace_bytes, void* stream) {
+  return bwd_bf16("fa_bwd", q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window,
+                  scale, workspace, workspace_bytes, nullptr, stream);
+}
+
+fa_status fa_bwd_alibi(const void* q, const void* k, const void* v, const void* o,
+                       const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                       void* workspace, size_t workspace_bytes, const float* alibi_slopes,
+                       void* stream) {
+  const fa_status st = need_slopes("fa_bwd_alibi", alibi_slopes);
   if (st != FA_OK) return st;
-  const size_t need = fa_bwd_workspace_size(B, Hq, Hkv, N, d, causal, window);
-  if (!workspace || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "fa_bwd: workspace of %zu bytes needed, %zu given", need,
-                workspace ? workspace_bytes : (size_t)0);
-  if (((uintptr_t)workspace & 255) != 0)
-    return fail(FA_ERR_WORKSPACE, "fa_bwd: workspace must be 256-byte aligned");
-  float* dvec = static_cast<float*>(workspace);
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, dvec, B, Hq, Hkv, N, d,
-                causal ? 1 : 0, window, scale, scale * fa::kHostLog2e, g_time_start,
-                g_time_stop};
-  g_time_start = g_time_stop = nullptr;
-  a.slopes = alibi_slopes;
-  return launched("fa_bwd", fa::launch_bwd_bf16(a, (hipStream_t)stream));
+  return bwd_bf16("fa_bwd_alibi", q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal,
+                  window, scale, workspace, workspace_bytes, alibi_slopes, stream);
 }
 
 fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
@@ -201,20 +299,19 @@ fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
 
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
-                        int Hkv, int d, int causal, int window, float scale,
-                        const float* alibi_slopes, void* stream) {
-  if (!q || !k || !v || !o || !lse)
-    return fail(FA_ERR_INVALID_ARG, "fa_fwd_varlen: null pointer");
-  fa_status st = check_varlen("fa_fwd_varlen", cu_seqlens, num_seqs, total, max_seqlen, Hq,
-                              Hkv, d, causal, window, scale);
-  if (st == FA_OK)
-    st = check_align("fa_fwd_varlen", {q, k, v, o}, {lse, cu_seqlens, alibi_slopes});
+                        int Hkv, int d, int causal, int window, float scale, void* stream) {
+  return fwd_varlen("fa_fwd_varlen", q, k, v, o, lse, cu_seqlens, num_seqs, total, max_seqlen,
+                    Hq, Hkv, d, causal, window, scale, nullptr, stream);
+}
+
+fa_status fa_fwd_varlen_alibi(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* cu_seqlens, int num_seqs, int total, int max_seqlen,
+                              int Hq, int Hkv, int d, int causal, int window, float scale,
+                              const float* alibi_slopes, void* stream) {
+  const fa_status st = need_slopes("fa_fwd_varlen_alibi", alibi_slopes);
   if (st != FA_OK) return st;
-  const float c2 = scale == 0.f ? 1e-30f : fabsf(scale) * fa::kHostLog2e;  // as in fa_fwd
-  fa::FwdArgs a{q, k, v, o, lse, num_seqs, Hq, Hkv, max_seqlen, d, causal ? 1 : 0, window,
-                c2, scale * fa::kHostLog2e, scale < 0.f ? 1 : 0, cu_seqlens, total};
-  a.slopes = alibi_slopes;
-  return launched("fa_fwd_varlen", fa::launch_fwd_bf16(a, (hipStream_t)stream));
+  return fwd_varlen("fa_fwd_varlen_alibi", q, k, v, o, lse, cu_seqlens, num_seqs, total,
+                    max_seqlen, Hq, Hkv, d, causal, window, scale, alibi_slopes, stream);
 }
 
 size_t fa_bwd_varlen_workspace_size(int total, int Hq, int Hkv, int d) {
@@ -228,27 +325,23 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         const void* dO, const float* lse, void* dq, void* dk, void* dv,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
                         int Hkv, int d, int causal, int window, float scale, void* workspace,
-                        size_t workspace_bytes, const float* alibi_slopes, void* stream) {
-  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
-    return fail(FA_ERR_INVALID_ARG, "fa_bwd_varlen: null pointer");
-  fa_status st = check_varlen("fa_bwd_varlen", cu_seqlens, num_seqs, total, max_seqlen, Hq,
-                              Hkv, d, causal, window, scale);
-  if (st == FA_OK)
-    st = check_align("fa_bwd_varlen", {q, k, v, o, dO, dq, dk, dv},
-                     {lse, cu_seqlens, alibi_slopes});
+                        size_t workspace_bytes, void* stream) {
+  return bwd_varlen("fa_bwd_varlen", q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, num_seqs,
+                    total, max_seqlen, Hq, Hkv, d, causal, window, scale, workspace,
+                    workspace_bytes, nullptr, stream);
+}
+
+fa_status fa_bwd_varlen_alibi(const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                              const int* cu_seqlens, int num_seqs, int total, int max_seqlen,
+                              int Hq, int Hkv, int d, int causal, int window, float scale,
+                              void* workspace, size_t workspace_bytes,
+                              const float* alibi_slopes, void* stream) {
+  const fa_status st = need_slopes("fa_bwd_varlen_alibi", alibi_slopes);
   if (st != FA_OK) return st;
-  const size_t need = fa_bwd_varlen_workspace_size(total, Hq, Hkv, d);
-  if (!workspace || workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "fa_bwd_varlen: workspace of %zu bytes needed, %zu given",
-                need, workspace ? workspace_bytes : (size_t)0);
-  if (((uintptr_t)workspace & 255) != 0)
-    return fail(FA_ERR_WORKSPACE, "fa_bwd_varlen: workspace must be 256-byte aligned");
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, static_cast<float*>(workspace), num_seqs, Hq,
-                Hkv, max_seqlen, d, causal ? 1 : 0, window, scale, scale * fa::kHostLog2e,
-                g_time_start, g_time_stop, cu_seqlens, total};
-  g_time_start = g_time_stop = nullptr;
-  a.slopes = alibi_slopes;
-  return launched("fa_bwd_varlen", fa::launch_bwd_bf16(a, (hipStream_t)stream));
+  return bwd_varlen("fa_bwd_varlen_alibi", q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens,
+                    num_seqs, total, max_seqlen, Hq, Hkv, d, causal, window, scale, workspace,
+                    workspace_bytes, alibi_slopes, stream);
 }
 
 int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
@@ -258,17 +351,20 @@ int fa_decode_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_
   if (num_splits > 0) return num_splits;
   // About one workgroup per compute unit (256 units; measured faster than two per unit,
   // with a shorter merge), chunks of at least 256 keys.
-  const long nrg = ((long)(Hq / Hkv) * Nq + 31) / 32;
-  const long base = (long)B * Hkv * nrg;
-  long s = (256 + base - 1) / base;
-  s = std::min<long>(s, std::max(1, Nk / 256));
-  s = std::min<long>(s, 64);
-  return (int)std::max<long>(s, 1);
+  const int64_t nrg = ((int64_t)(Hq / Hkv) * Nq + 31) / 32;  // < 2^58: no overflow
+  const int64_t base = sat_mul({B, Hkv, nrg});
+  int64_t s = (256 + base - 1) / base;
+  s = std::min<int64_t>(s, std::max(1, Nk / 256));
+  s = std::min<int64_t>(s, 64);
+  return (int)std::max<int64_t>(s, 1);
 }
 
 size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int num_splits) {
   const int S = fa_decode_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits);
   if (S <= 1) return 0;
+  // fa_decode accepts only B * Nq * Hq * d < 2^31, so the partial outputs of S <= 256 chunks
+  // stay far below size_t's range; larger sizes report 0 (the call itself would be rejected)
+  if (sat_mul({B, Nq, Hq, d}) >= kMaxElems) return 0;
   const size_t rows = (size_t)S * B * Hq * Nq;
   return align256(rows * d * sizeof(float)) + align256(rows * sizeof(float));
 }
@@ -285,13 +381,13 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache,
   if (st != FA_OK) return st;
   if (d != 64 && d != 128)
     return fail(FA_ERR_UNSUPPORTED, "fa_decode: head dim %d not supported (64 or 128)", d);
-  if ((int64_t)B * Nq * Hq * d >= kMaxElems)
-    return fail(FA_ERR_INVALID_ARG, "fa_decode: B*Nq*Hq*d exceeds 2^31");
+  if (sat_mul({B, Nq, Hq, d}) >= kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "fa_decode: B*Nq*Hq*d reaches 2^31");
   if (num_splits < 0 || num_splits > kMaxSplits)
     return fail(FA_ERR_INVALID_ARG, "fa_decode: num_splits=%d outside [0, %d]", num_splits,
                 kMaxSplits);
   const int S = fa_decode_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits);
-  if ((int64_t)B * Hkv * ((Hq / Hkv * Nq + 31) / 32) * S >= kMaxElems)
+  if (sat_mul({B, Hkv, ((int64_t)(Hq / Hkv) * Nq + 31) / 32, S}) >= kMaxElems)
     return fail(FA_ERR_INVALID_ARG, "fa_decode: grid too large");
   const size_t need = fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits);
   if (need > 0 && (!workspace || workspace_bytes < need))

@@ -1,11 +1,12 @@
 """Thin ctypes binding of libfa.so (argument marshalling only).
 
-The functions ``fa_fwd``, ``fa_fwd_fp32``, ``fa_bwd``, ``fa_bwd_workspace_size``,
-``fa_last_error`` and ``fa_version`` mirror the C entry points of ``include/fa.h`` one to
-one; they take torch tensors only as carriers of device pointers and of the current HIP
-stream.  ``forward`` / ``backward`` add output allocation for convenience.  Every step of
-the computation runs in the HIP kernels of libfa.so: when the library is missing, loading
-raises instead of falling back to anything else.
+The functions named ``fa_*`` (``fa_fwd``, ``fa_fwd_alibi``, ``fa_fwd_fp32``, ``fa_bwd``,
+``fa_bwd_workspace_size``, ...) mirror the C entry points of ``include/fa.h`` one to one,
+in the same argument order; they take torch tensors only as carriers of device pointers and
+of the current HIP stream.  ``forward`` / ``backward`` (and their packed-sequence and decoding
+counterparts) check the tensors and allocate outputs for convenience.  Every step of the
+computation runs in the HIP kernels of libfa.so: when the library is missing, loading raises
+instead of falling back to anything else.
 """
 
 from __future__ import annotations
@@ -21,9 +22,10 @@ _lib = None
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 
-EXPORTED = ("fa_fwd", "fa_fwd_fp32", "fa_fwd_fp8", "fa_decode", "fa_decode_num_splits",
-            "fa_decode_workspace_size", "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_varlen",
-            "fa_bwd_varlen", "fa_bwd_varlen_workspace_size", "fa_bwd_time_main_kernel",
+EXPORTED = ("fa_fwd", "fa_fwd_alibi", "fa_fwd_fp32", "fa_fwd_fp8", "fa_decode",
+            "fa_decode_num_splits", "fa_decode_workspace_size", "fa_bwd", "fa_bwd_alibi",
+            "fa_bwd_workspace_size", "fa_fwd_varlen", "fa_fwd_varlen_alibi", "fa_bwd_varlen",
+            "fa_bwd_varlen_alibi", "fa_bwd_varlen_workspace_size", "fa_bwd_time_main_kernel",
             "fa_mfma_probe", "fa_last_error", "fa_version")
 
 
@@ -47,24 +49,33 @@ def load() -> ctypes.CDLL:
                            "`python -m exact_io_aware_fa2_amd.build` (no fallback exists)")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp]
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_alibi.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, vp]
+    lib.fa_fwd_alibi.restype = i
     lib.fa_fwd_fp32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp32.restype = i
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, f, f, f, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = i
     lib.fa_bwd_workspace_size.argtypes = [i, i, i, i, i, i, i]
     lib.fa_bwd_workspace_size.restype = sz
-    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp,
-                           vp]
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_bwd.restype = i
-    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, vp]
+    lib.fa_bwd_alibi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp,
+                                 sz, vp, vp]
+    lib.fa_bwd_alibi.restype = i
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_varlen.restype = i
+    lib.fa_fwd_varlen_alibi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, vp]
+    lib.fa_fwd_varlen_alibi.restype = i
     lib.fa_bwd_varlen_workspace_size.argtypes = [i, i, i, i]
     lib.fa_bwd_varlen_workspace_size.restype = sz
     lib.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i,
-                                  i, f, vp, sz, vp, vp]
+                                  i, f, vp, sz, vp]
     lib.fa_bwd_varlen.restype = i
+    lib.fa_bwd_varlen_alibi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                        i, i, f, vp, sz, vp, vp]
+    lib.fa_bwd_varlen_alibi.restype = i
     lib.fa_decode_num_splits.argtypes = [i, i, i, i, i, i, i]
     lib.fa_decode_num_splits.restype = i
     lib.fa_decode_workspace_size.argtypes = [i, i, i, i, i, i, i]
@@ -105,11 +116,16 @@ def _check(status: int):
 
 
 # ------------------------------------------------------------ 1:1 C entry points
-def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, stream=None,
-           alibi_slopes=None) -> int:
+def fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, stream=None) -> int:
     return load().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
-                         int(causal), int(window), float(scale), _ptr(alibi_slopes),
-                         _stream(stream))
+                         int(causal), int(window), float(scale), _stream(stream))
+
+
+def fa_fwd_alibi(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, window, scale, alibi_slopes,
+                 stream=None) -> int:
+    return load().fa_fwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, d,
+                               int(causal), int(window), float(scale), _ptr(alibi_slopes),
+                               _stream(stream))
 
 
 def fa_fwd_fp8(q, k, v, o, lse, descale_q, descale_k, descale_v, B, Hq, Hkv, N, d, causal,
@@ -129,18 +145,33 @@ def fa_bwd_workspace_size(B, Hq, Hkv, N, d, causal, window) -> int:
 
 
 def fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
-           workspace, workspace_bytes, stream=None, alibi_slopes=None) -> int:
+           workspace, workspace_bytes, stream=None) -> int:
     return load().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq),
                          _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal), int(window),
-                         float(scale), _ptr(workspace), int(workspace_bytes),
-                         _ptr(alibi_slopes), _stream(stream))
+                         float(scale), _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_bwd_alibi(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
+                 workspace, workspace_bytes, alibi_slopes, stream=None) -> int:
+    return load().fa_bwd_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                               _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal),
+                               int(window), float(scale), _ptr(workspace),
+                               int(workspace_bytes), _ptr(alibi_slopes), _stream(stream))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, total, max_seqlen, Hq, Hkv, d, causal,
-                  window, scale, stream=None, alibi_slopes=None) -> int:
+                  window, scale, stream=None) -> int:
     return load().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens),
                                 num_seqs, total, max_seqlen, Hq, Hkv, d, int(causal),
-                                int(window), float(scale), _ptr(alibi_slopes), _stream(stream))
+                                int(window), float(scale), _stream(stream))
+
+
+def fa_fwd_varlen_alibi(q, k, v, o, lse, cu_seqlens, num_seqs, total, max_seqlen, Hq, Hkv, d,
+                        causal, window, scale, alibi_slopes, stream=None) -> int:
+    return load().fa_fwd_varlen_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                      _ptr(cu_seqlens), num_seqs, total, max_seqlen, Hq, Hkv, d,
+                                      int(causal), int(window), float(scale),
+                                      _ptr(alibi_slopes), _stream(stream))
 
 
 def fa_bwd_varlen_workspace_size(total, Hq, Hkv, d) -> int:
@@ -148,13 +179,21 @@ def fa_bwd_varlen_workspace_size(total, Hq, Hkv, d) -> int:
 
 
 def fa_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, num_seqs, total, max_seqlen, Hq,
-                  Hkv, d, causal, window, scale, workspace, workspace_bytes, stream=None,
-                  alibi_slopes=None) -> int:
+                  Hkv, d, causal, window, scale, workspace, workspace_bytes, stream=None) -> int:
     return load().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), num_seqs, total,
                                 max_seqlen, Hq, Hkv, d, int(causal), int(window), float(scale),
-                                _ptr(workspace), int(workspace_bytes), _ptr(alibi_slopes),
-                                _stream(stream))
+                                _ptr(workspace), int(workspace_bytes), _stream(stream))
+
+
+def fa_bwd_varlen_alibi(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, num_seqs, total, max_seqlen,
+                        Hq, Hkv, d, causal, window, scale, workspace, workspace_bytes,
+                        alibi_slopes, stream=None) -> int:
+    return load().fa_bwd_varlen_alibi(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                                      _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens), num_seqs,
+                                      total, max_seqlen, Hq, Hkv, d, int(causal), int(window),
+                                      float(scale), _ptr(workspace), int(workspace_bytes),
+                                      _ptr(alibi_slopes), _stream(stream))
 
 
 def fa_decode_num_splits(B, Hq, Hkv, Nq, Nk, d, num_splits) -> int:
@@ -223,15 +262,28 @@ def _same_dtype_device(*ts):
         raise ValueError("q, k and v must share one dtype and one device")
 
 
-def _slopes(alibi_slopes, Hq):
-    """Check an optional ALiBi slope tensor: float32, contiguous, on the device, Hq values."""
+def _slopes(alibi_slopes, Hq, device):
+    """Check an optional ALiBi slope tensor: float32, contiguous, Hq values, on the inputs'
+    device."""
     if alibi_slopes is None:
         return None
     t = alibi_slopes
     if (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()
-            or t.numel() != Hq):
-        raise ValueError(f"alibi_slopes must be a contiguous float32 device tensor of {Hq} "
-                         "slopes (one per query head)")
+            or t.numel() != Hq or t.device != device):
+        raise ValueError(f"alibi_slopes must be a contiguous float32 tensor of {Hq} slopes "
+                         f"(one per query head) on {device}")
+    return t
+
+
+def _device_buffer(t, name, device, nbytes=None):
+    """A caller-supplied raw buffer (workspace): contiguous, on the inputs' device, and at
+    least ``nbytes`` bytes when given.  The C layer checks only size and alignment, so a host
+    tensor here would hand a host address to the kernels."""
+    if not t.is_cuda or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous tensor on {device}; got "
+                         f"{'contiguous' if t.is_contiguous() else 'non-contiguous'} on {t.device}")
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, {nbytes} needed")
     return t
 
 
@@ -245,8 +297,12 @@ def forward(q, k, v, causal=False, window=0, scale=None, out=None, lse=None, str
     lse = (torch.empty((B, Hq, N), device=q.device, dtype=torch.float32) if lse is None
            else _expect(lse, "lse", (B, Hq, N), torch.float32, q.device))
     if q.dtype == torch.bfloat16:
-        _check(fa_fwd(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, stream,
-                      _slopes(alibi_slopes, Hq)))
+        sl = _slopes(alibi_slopes, Hq, q.device)
+        if sl is None:
+            _check(fa_fwd(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, stream))
+        else:
+            _check(fa_fwd_alibi(q, k, v, out, lse, B, Hq, Hkv, N, d, causal, window, scale, sl,
+                                stream))
     elif q.dtype == torch.float32:
         if alibi_slopes is not None:
             raise ValueError("the float32 forward has no position bias")
@@ -298,11 +354,17 @@ def backward(q, k, v, o, dO, lse, causal=False, window=0, scale=None, dq=None, d
     dq = torch.empty_like(q) if dq is None else _expect(dq, "dq", q.shape, q.dtype, dev)
     dk = torch.empty_like(k) if dk is None else _expect(dk, "dk", k.shape, k.dtype, dev)
     dv = torch.empty_like(v) if dv is None else _expect(dv, "dv", v.shape, v.dtype, dev)
+    sl = _slopes(alibi_slopes, Hq, dev)
     if workspace is None:
         workspace = workspace_for(B, Hq, Hkv, N, d, causal, window, q.device)
-    _check(fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
-                  workspace, workspace.numel() * workspace.element_size(), stream,
-                  _slopes(alibi_slopes, Hq)))
+    _device_buffer(workspace, "workspace", dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    if sl is None:
+        _check(fa_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
+                      workspace, nbytes, stream))
+    else:
+        _check(fa_bwd_alibi(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window,
+                            scale, workspace, nbytes, sl, stream))
     return dq, dk, dv
 
 
@@ -337,8 +399,13 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen, causal=False, window=0, scal
     out = torch.empty_like(q) if out is None else _expect(out, "out", q.shape, q.dtype, q.device)
     lse = (torch.empty((Hq, T), device=q.device, dtype=torch.float32) if lse is None
            else _expect(lse, "lse", (Hq, T), torch.float32, q.device))
-    _check(fa_fwd_varlen(q, k, v, out, lse, cu_seqlens, S, T, max_seqlen, Hq, Hkv, d, causal,
-                         window, scale, stream, _slopes(alibi_slopes, Hq)))
+    sl = _slopes(alibi_slopes, Hq, q.device)
+    if sl is None:
+        _check(fa_fwd_varlen(q, k, v, out, lse, cu_seqlens, S, T, max_seqlen, Hq, Hkv, d, causal,
+                             window, scale, stream))
+    else:
+        _check(fa_fwd_varlen_alibi(q, k, v, out, lse, cu_seqlens, S, T, max_seqlen, Hq, Hkv, d,
+                                   causal, window, scale, sl, stream))
     return out, lse
 
 
@@ -362,12 +429,18 @@ def backward_varlen(q, k, v, o, dO, lse, cu_seqlens, max_seqlen, causal=False, w
     dq = torch.empty_like(q) if dq is None else _expect(dq, "dq", q.shape, q.dtype, dev)
     dk = torch.empty_like(k) if dk is None else _expect(dk, "dk", k.shape, k.dtype, dev)
     dv = torch.empty_like(v) if dv is None else _expect(dv, "dv", v.shape, v.dtype, dev)
+    sl = _slopes(alibi_slopes, Hq, dev)
     if workspace is None:
         workspace = workspace_for_varlen(T, Hq, Hkv, d, q.device)
-    _check(fa_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, S, T, max_seqlen, Hq, Hkv,
-                         d, causal, window, scale, workspace,
-                         workspace.numel() * workspace.element_size(), stream,
-                         _slopes(alibi_slopes, Hq)))
+    _device_buffer(workspace, "workspace", dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    if sl is None:
+        _check(fa_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, S, T, max_seqlen, Hq,
+                             Hkv, d, causal, window, scale, workspace, nbytes, stream))
+    else:
+        _check(fa_bwd_varlen_alibi(q, k, v, o, dO, lse, dq, dk, dv, cu_seqlens, S, T, max_seqlen,
+                                   Hq, Hkv, d, causal, window, scale, workspace, nbytes, sl,
+                                   stream))
     return dq, dk, dv
 
 
@@ -385,8 +458,9 @@ def decode(q, k_cache, v_cache, seqlens_k=None, causal=True, window=0, scale=Non
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("q and the caches must be contiguous bf16 device tensors")
     if seqlens_k is not None and (seqlens_k.dtype != torch.int32 or seqlens_k.numel() != B
-                                  or not seqlens_k.is_cuda):
-        raise ValueError("seqlens_k must be an int32 device tensor of B lengths")
+                                  or not seqlens_k.is_cuda or seqlens_k.device != q.device
+                                  or not seqlens_k.is_contiguous()):
+        raise ValueError(f"seqlens_k must be a contiguous int32 tensor of B lengths on {q.device}")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     if any(t.device != q.device for t in (k_cache, v_cache)):
         raise ValueError("q and the caches must be on one device")
@@ -396,6 +470,8 @@ def decode(q, k_cache, v_cache, seqlens_k=None, causal=True, window=0, scale=Non
     nbytes = fa_decode_workspace_size(B, Hq, Hkv, Nq, Nk, d, num_splits)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _device_buffer(workspace, "workspace", q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(fa_decode(q, k_cache, v_cache, seqlens_k, out, lse, B, Hq, Hkv, Nq, Nk, d, causal,
                      window, scale, num_splits, workspace, wbytes, stream))

@@ -25,13 +25,14 @@
  *   window == 0 : no window
  * A masked entry has probability zero: it never enters the normaliser.
  *
- * Position bias (bmjup.com page, FAQ on inference: the alibi_slopes argument, no bias when
- * it is None; hysenlabs.com page, hardware-boundary section: ALiBi): fa_fwd, fa_bwd,
- * fa_fwd_varlen and fa_bwd_varlen take `alibi_slopes`, NULL for none or a device array of
- * Hq float32 slopes m_h (caller-owned, read by the kernels only, used as given, any finite
- * value).  Query head h then scores s_ij = scale * q_i . k_j - m_h * |i - j| before the
- * mask and the softmax, with positions counted from the start of each sequence; lse is
- * the logsumexp of those biased scores, and the backward treats the slopes as constants.
+ * Position bias (bmjup.com page, FAQ on inference: an optional alibi_slopes argument, no
+ * bias when it is absent; hysenlabs.com page, hardware-boundary section: ALiBi): the
+ * *_alibi entry points take a device array `alibi_slopes` of Hq float32 slopes m_h
+ * (caller-owned, read by the kernels only, used as given, any finite value; NULL is
+ * rejected: the plain entry points are the no-bias case).  Query head h then scores
+ * s_ij = scale * q_i . k_j - m_h * |i - j| before the mask and the softmax, with positions
+ * counted from the start of each sequence; lse is the logsumexp of those biased scores, and
+ * the backward treats the slopes as constants.
  *
  * Conventions for every entry point:
  *   - The caller owns every buffer (device memory, e.g. from hipMalloc or a framework
@@ -40,7 +41,10 @@
  *     Results are valid once the stream has reached that point.
  *   - Arguments are validated before anything is launched.  On a non-FA_OK status
  *     nothing was enqueued and fa_last_error() describes the problem.
- *   - Stateless and re-entrant; the only state is the thread-local error message.
+ *   - Re-entrant.  The library keeps no state between calls except two thread-local items:
+ *     the message of the last error and a pending timing request (fa_bwd_time_main_kernel,
+ *     a benchmark hook that only the next backward or decode call on the same thread reads
+ *     and clears).
  *   - Output buffers must not alias input buffers.
  *   - Tensor pointers (q, k, v, o, dO, dq, dk, dv, the caches) must be 16-byte aligned
  *     and the float32 / int32 arrays (lse, cu_seqlens, seqlens_k, alibi_slopes) 4-byte
@@ -76,7 +80,15 @@ typedef enum {
  */
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                  int Hq, int Hkv, int N, int d, int causal, int window, float scale,
-                 const float* alibi_slopes, void* stream);
+                 void* stream);
+
+/*
+ * fa_fwd with the ALiBi position bias (see the header comment): `alibi_slopes` is a device
+ * array of Hq float32 slopes; NULL returns FA_ERR_INVALID_ARG.  Other rules as fa_fwd.
+ */
+fa_status fa_fwd_alibi(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                       const float* alibi_slopes, void* stream);
 
 /*
  * Forward with 8-bit inputs.  The pages name an FP8 forward pass of a later version of the
@@ -105,7 +117,10 @@ fa_status fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Forward, float32 in and out (same contract and layouts as fa_fwd, every tensor float32).
- * Dot products, softmax and accumulation are all float32.
+ * Dot products, softmax and accumulation are all float32.  The pages name float32 inputs
+ * as a data type of the ROCm Triton backend only (hysenlabs.com, "dao-ailab
+ * flash-attention", hardware-boundary section; the CUDA build takes fp16 / bf16 only,
+ * bmjup.com page, section 4); this entry point is that float32 forward.
  */
 fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, float* lse,
                       int B, int Hq, int Hkv, int N, int d, int causal, int window,
@@ -113,8 +128,11 @@ fa_status fa_fwd_fp32(const float* q, const float* k, const float* v, float* o, 
 
 /*
  * Bytes of device workspace fa_bwd needs for these sizes: D = rowsum(dO * O) as float32
- * [B, Hq, N], rounded up to a multiple of 256 bytes.  Linear in N.  Returns 0 for arguments
- * fa_bwd would reject.
+ * [B, Hq, N], rounded up to a multiple of 256 bytes.  Linear in N: the backward keeps one
+ * float per query row besides its inputs and outputs, never an N x N matrix (ainews.cool,
+ * "flash-attention transformer optimization", technical deep dive: item 2, recomputation
+ * instead of storing the attention matrix, and the memory table, linear growth with the
+ * sequence length).  Returns 0 for arguments fa_bwd would reject.
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, int window);
 
@@ -136,7 +154,14 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int N, int d, int causal, i
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
                  const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
                  int N, int d, int causal, int window, float scale, void* workspace,
-                 size_t workspace_bytes, const float* alibi_slopes, void* stream);
+                 size_t workspace_bytes, void* stream);
+
+/* fa_bwd for the forward of fa_fwd_alibi (the same slopes); NULL slopes are rejected. */
+fa_status fa_bwd_alibi(const void* q, const void* k, const void* v, const void* o,
+                       const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                       int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                       void* workspace, size_t workspace_bytes, const float* alibi_slopes,
+                       void* stream);
 
 /*
  * Packed variable-length sequences.  bmjup.com, "FlashAttention-2 ... 实战解析", FAQ Q4,
@@ -160,8 +185,14 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
  */
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
-                        int Hkv, int d, int causal, int window, float scale,
-                        const float* alibi_slopes, void* stream);
+                        int Hkv, int d, int causal, int window, float scale, void* stream);
+
+/* Packed sequences with the ALiBi position bias (positions counted from each sequence's
+ * first row); NULL slopes are rejected. */
+fa_status fa_fwd_varlen_alibi(const void* q, const void* k, const void* v, void* o, float* lse,
+                              const int* cu_seqlens, int num_seqs, int total, int max_seqlen,
+                              int Hq, int Hkv, int d, int causal, int window, float scale,
+                              const float* alibi_slopes, void* stream);
 
 /* Workspace bytes for fa_bwd_varlen: D as float32 [Hq, total] rounded up to 256; 0 for
  * invalid sizes. */
@@ -171,7 +202,14 @@ fa_status fa_bwd_varlen(const void* q, const void* k, const void* v, const void*
                         const void* dO, const float* lse, void* dq, void* dk, void* dv,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
                         int Hkv, int d, int causal, int window, float scale, void* workspace,
-                        size_t workspace_bytes, const float* alibi_slopes, void* stream);
+                        size_t workspace_bytes, void* stream);
+
+fa_status fa_bwd_varlen_alibi(const void* q, const void* k, const void* v, const void* o,
+                              const void* dO, const float* lse, void* dq, void* dk, void* dv,
+                              const int* cu_seqlens, int num_seqs, int total, int max_seqlen,
+                              int Hq, int Hkv, int d, int causal, int window, float scale,
+                              void* workspace, size_t workspace_bytes,
+                              const float* alibi_slopes, void* stream);
 
 /*
  * Decoding: the newest queries of each sequence over its KV cache, the method at inference
@@ -204,8 +242,8 @@ fa_status fa_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Benchmark hook (no counterpart on the pages): the next fa_bwd, fa_bwd_varlen or fa_decode
- * call made on this thread records `start_event` on its stream right before its main kernel
+ * Benchmark hook (no counterpart on the pages): the next backward (fa_bwd, fa_bwd_alibi,
+ * fa_bwd_varlen, fa_bwd_varlen_alibi) or fa_decode call made on this thread records `start_event` on its stream right before its main kernel
  * (the key-block kernel for dK, dV; the chunk kernel of fa_decode) and `stop_event` right
  * after it (the dQ kernel, or the chunk merge, follows), so a caller can time the kernels
  * separately with hipEventElapsedTime.  Arguments are hipEvent_t handles owned by the caller; passing NULL

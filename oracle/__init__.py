@@ -39,9 +39,10 @@ from .attention import (  # noqa: F401
     attn_fwd_rows,
     attn_bwd_dq_rows,
     attn_bwd_dkdv_cols,
+    attn_bwd_dkdv_cols_from_fwd,
     attended_pairs,
     attn_fwd_varlen,
     attn_bwd_varlen,
     attn_decode,
 )
-from .fp8 import attn_fwd_fp8, attn_fwd_fp8_rows, dequantize, e4m3_decode  # noqa: F401
+from .fp8 import attn_fwd_fp8, dequantize, e4m3_decode  # noqa: F401

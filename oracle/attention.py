@@ -266,6 +266,44 @@ def attn_bwd_dkdv_cols(q, k, v, do, cols, causal=False, window=0, scale=None,
     return dk, dv
 
 
+def attn_bwd_dkdv_cols_from_fwd(q, k, v, do, o, lse, cols, causal=False, window=0, scale=None,
+                                row_chunk=DEFAULT_ROW_CHUNK, slope=0.0):
+    """Like ``attn_bwd_dkdv_cols``, but from this head's forward outputs O and LSE (of this
+    same oracle) instead of whole softmax rows.
+
+    The probability of an allowed pair is P_ij = exp(s_ij - LSE_i) (LSE_i is the row's
+    natural-log normaliser, so this is the softmax itself), and D_i = sum_c dO_ic O_ic equals
+    sum_j P_ij dP_ij; with them only the selected key columns are needed (ainews.cool
+    "flash-attention transformer optimization", technical deep dive, item 2: the matrix is
+    rebuilt from what the forward kept).  Cost is linear in the number of rows, so the heavy
+    key blocks of very long sequences can be checked.  q [N, d], k/v [Nk, d], do/o [N, dv],
+    lse [N]; returns this query head's dK, dV at ``cols``.
+    """
+    q, k, v, do, o = _as64(q), _as64(k), _as64(v), _as64(do), _as64(o)
+    lse = _as64(lse)
+    scale = 1.0 / math.sqrt(q.shape[1]) if scale is None else float(scale)
+    cols = np.asarray(cols, dtype=np.int64)
+    n = q.shape[0]
+    r0 = int(cols.min()) if causal else 0
+    r1 = min(n, int(cols.max()) + window) if window > 0 else n
+    dk = np.zeros((cols.size, k.shape[1]))
+    dv = np.zeros((cols.size, v.shape[1]))
+    kc, vc = k[cols], v[cols]
+    for a in range(r0, r1, row_chunk):
+        rows = np.arange(a, min(r1, a + row_chunk))
+        s = scale * (q[rows] @ kc.T)
+        if slope:
+            s = s - slope * np.abs(rows[:, None] - cols[None, :]).astype(np.float64)
+        ok = _mask(rows, cols, causal, window) & np.isfinite(lse[rows])[:, None]
+        p = np.where(ok, np.exp(np.where(ok, s - lse[rows][:, None], 0.0)), 0.0)
+        dp = do[rows] @ vc.T
+        dvec = (do[rows] * o[rows]).sum(axis=1)
+        ds = p * (dp - dvec[:, None])
+        dk += scale * (ds.T @ q[rows])
+        dv += p.T @ do[rows]
+    return dk, dv
+
+
 # ------------------------------------------------------------------ full tensors
 def _check_shapes(q, k, v):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:

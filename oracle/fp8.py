@@ -24,7 +24,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import attn_fwd, attn_fwd_rows
+from .attention import attn_fwd
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -53,9 +53,3 @@ def attn_fwd_fp8(q8, k8, v8, descale_q, descale_k, descale_v, causal=False, wind
     return attn_fwd(dequantize(q8, descale_q), dequantize(k8, descale_k),
                     dequantize(v8, descale_v), causal, window, scale, **kw)
 
-
-def attn_fwd_fp8_rows(q8, k8, v8, descale_q, descale_k, descale_v, rows, causal=False,
-                      window=0, scale=None):
-    """O and LSE of one head for the selected query ``rows`` (q8 [N, d], k8 / v8 [N, d])."""
-    return attn_fwd_rows(dequantize(q8, descale_q), dequantize(k8, descale_k),
-                         dequantize(v8, descale_v), rows, causal, window, scale)

@@ -46,6 +46,18 @@ def workers() -> int:
     return max(1, min(16, n))
 
 
+def pool_map(fn, tasks):
+    """fn over tasks in a pool of workers() spawned processes, one BLAS thread each (fn must
+    be a module-level function); results in task order."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+
+    import oracle.attention as oa
+    with ProcessPoolExecutor(max_workers=workers(), mp_context=mp.get_context("spawn"),
+                             initializer=oa._limit_blas_threads) as ex:
+        return list(ex.map(fn, tasks))
+
+
 def to64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 

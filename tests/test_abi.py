@@ -4,6 +4,8 @@ validates arguments before launching anything, and sizes its workspace linearly 
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -233,8 +235,17 @@ def _misaligned_calls(t16, t4):
                                             0, 0.125, stream=0),
         "fa_bwd": lambda: fa.fa_bwd(A, A, A, A, A, t4, A, A, t16, 1, 2, 2, 16, 64, 0, 0, 0.125,
                                     A, 1 << 20, stream=0),
+        "fa_fwd_alibi": lambda: fa.fa_fwd_alibi(A, t16, A, A, A, 1, 2, 2, 16, 64, 1, 0, 0.125,
+                                                t4, stream=0),
+        "fa_bwd_alibi": lambda: fa.fa_bwd_alibi(A, A, A, t16, A, A, A, A, A, 1, 2, 2, 16, 64, 1,
+                                                0, 0.125, A, 1 << 20, t4, stream=0),
         "fa_fwd_varlen": lambda: fa.fa_fwd_varlen(A, A, t16, A, t4, A, 1, 16, 16, 2, 2, 64, 0, 0,
                                                   0.125, stream=0),
+        "fa_fwd_varlen_alibi": lambda: fa.fa_fwd_varlen_alibi(A, A, A, t16, A, A, 1, 16, 16, 2,
+                                                              2, 64, 0, 0, 0.125, t4, stream=0),
+        "fa_bwd_varlen_alibi": lambda: fa.fa_bwd_varlen_alibi(A, A, A, A, A, A, t16, A, A, t4, 1,
+                                                              16, 16, 2, 2, 64, 0, 0, 0.125, A,
+                                                              1 << 20, A, stream=0),
         "fa_bwd_varlen": lambda: fa.fa_bwd_varlen(A, A, A, A, t16, t4, A, A, A, A, 1, 16, 16, 2,
                                                   2, 64, 0, 0, 0.125, A, 1 << 20, stream=0),
         "fa_decode": lambda: fa.fa_decode(A, A, t16, None, A, t4, 1, 2, 2, 1, 16, 64, 1, 0, 0.125,
@@ -263,3 +274,127 @@ def test_python_buffer_checks():
         fa._expect(t.t(), "x", (3, 2), torch.float32, t.device)  # not contiguous
     with pytest.raises(ValueError, match="one dtype"):
         fa._same_dtype_device(t, t.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("entry", ["fa_fwd_alibi", "fa_bwd_alibi", "fa_fwd_varlen_alibi",
+                                   "fa_bwd_varlen_alibi"])
+def test_alibi_entry_points_need_slopes(entry):
+    A = _A
+    calls = {
+        "fa_fwd_alibi": lambda s: fa.fa_fwd_alibi(A, A, A, A, A, 1, 2, 2, 16, 64, 1, 0, 0.125, s,
+                                                  stream=0),
+        "fa_bwd_alibi": lambda s: fa.fa_bwd_alibi(A, A, A, A, A, A, A, A, A, 1, 2, 2, 16, 64, 1,
+                                                  0, 0.125, A, 1 << 20, s, stream=0),
+        "fa_fwd_varlen_alibi": lambda s: fa.fa_fwd_varlen_alibi(A, A, A, A, A, A, 1, 16, 16, 2,
+                                                                2, 64, 1, 0, 0.125, s, stream=0),
+        "fa_bwd_varlen_alibi": lambda s: fa.fa_bwd_varlen_alibi(A, A, A, A, A, A, A, A, A, A, 1,
+                                                                16, 16, 2, 2, 64, 1, 0, 0.125, A,
+                                                                1 << 20, s, stream=0),
+    }
+    assert calls[entry](None) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_last_error().startswith(entry) and "alibi_slopes" in fa.fa_last_error()
+    # the other checks still run first on a call that has its slopes
+    assert calls[entry](A + 2) == fa.FA_ERR_INVALID_ARG and "aligned" in fa.fa_last_error()
+
+
+def test_python_workspace_and_slope_checks():
+    """The binding rejects a host workspace (its address would reach the kernels), a
+    non-contiguous one, and slopes that are not on the inputs' device."""
+    import torch
+    dev = torch.device("cuda", 0)  # a device object only: nothing is allocated on it
+    host = torch.empty(1024, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="workspace must be a contiguous tensor on cuda:0"):
+        fa._device_buffer(host, "workspace", dev)
+    with pytest.raises(ValueError, match="non-contiguous"):
+        fa._device_buffer(host[::2], "workspace", dev)
+    assert fa._slopes(None, 4, dev) is None
+    with pytest.raises(ValueError, match="alibi_slopes"):
+        fa._slopes(torch.ones(4), 4, dev)
+
+
+def _cc():
+    return shutil.which("gcc") or shutil.which("cc")
+
+
+@pytest.mark.skipif(_cc() is None, reason="no C compiler")
+def test_c_caller_compiled_against_the_header(tmp_path):
+    """A plain C program built against include/fa.h: the contract prototypes, written out on
+    their own, must accept every library function (a mismatch fails the build), and every
+    rejected call returns its status through the C ABI."""
+    src = os.path.join(ROOT, "tests", "abi_caller.c")
+    pkg = os.path.dirname(fa.lib_path())
+    cmd = [_cc(), "-std=c11", "-Wall", "-Werror=incompatible-pointer-types",
+           "-I", os.path.join(ROOT, "include"), None, "-L", pkg, "-l:libfa.so",
+           f"-Wl,-rpath,{pkg}", "-Wl,-rpath-link,/opt/rocm/lib", "-o", None]
+    exe = str(tmp_path / "abi_caller")
+    build = subprocess.run([src if c is None and i < 8 else exe if c is None else c
+                            for i, c in enumerate(cmd)], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert run.returncode == 0 and "abi_caller ok" in run.stdout, run.stdout + run.stderr
+    # the prototype pin bites: a caller that expects the bias argument in fa_fwd does not build
+    text = open(src).read()
+    bad = text.replace("int, int, int, int, float, void*);\ntypedef fa_status (*fwd_fp32_fn)",
+                       "int, int, int, int, float, const float*, void*);\n"
+                       "typedef fa_status (*fwd_fp32_fn)", 1)
+    assert bad != text
+    bad_src = tmp_path / "bad_caller.c"
+    bad_src.write_text(bad)
+    res = subprocess.run([str(bad_src) if c is None and i < 8 else exe + "_bad" if c is None
+                          else c for i, c in enumerate(cmd)], capture_output=True, text=True)
+    assert res.returncode != 0 and "incompatible" in res.stderr
+
+
+def _hipcc():
+    c = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    return c if os.path.exists(c) else None
+
+
+@pytest.mark.skipif(_hipcc() is None, reason="hipcc not found")
+def test_api_layer_under_host_sanitizers(tmp_path):
+    """fa_api.hip's validation and argument marshalling built for the host with
+    AddressSanitizer and UndefinedBehaviorSanitizer (device code is not built), linked with
+    launchers that record their arguments instead of launching: valid calls must derive the
+    right launch arguments, rejected calls (including int sizes whose products overflow
+    64 bits) must launch nothing, and no sanitizer may fire."""
+    san = []
+    for f in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+              "-fno-omit-frame-pointer"):
+        san += ["-Xarch_host", f]
+    base = [_hipcc(), "--offload-arch=gfx950", "--cuda-host-only", "-O1", "-g", "-std=c++17"]
+    objs = []
+    for src, extra in ((os.path.join(ROOT, "exact_io_aware_fa2_amd", "csrc", "fa_api.hip"), []),
+                       (os.path.join(ROOT, "tests", "native", "stub_launchers.cpp"), ["-x", "hip"]),
+                       (os.path.join(ROOT, "tests", "native", "api_sanitize.cpp"), ["-x", "hip"])):
+        obj = str(tmp_path / (os.path.basename(src) + ".o"))
+        res = subprocess.run(base + extra + san + ["-c", src, "-o", obj], capture_output=True,
+                             text=True)
+        assert res.returncode == 0, res.stderr
+        objs.append(obj)
+    exe = str(tmp_path / "api_sanitize")
+    res = subprocess.run([_hipcc()] + san + objs + ["-o", exe], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=300, env=env)
+    assert run.returncode == 0 and "api_sanitize ok" in run.stdout, run.stdout + run.stderr
+    assert "runtime error" not in run.stderr and "AddressSanitizer" not in run.stderr
+
+
+def test_library_never_allocates_frees_or_synchronises():
+    """The memory claim of the boundary (every buffer is the caller's; the backward keeps
+    O(N) state in the caller's workspace, ainews.cool "flash-attention transformer
+    optimization", technical deep dive, memory table): libfa.so imports no HIP allocation,
+    free or synchronisation routine at all."""
+    nm = shutil.which("nm") or shutil.which("llvm-nm")
+    if nm is None:
+        pytest.skip("nm not found")
+    out = subprocess.run([nm, "-D", "--undefined-only", fa.lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    imported = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    hip = sorted(n for n in imported if n.startswith("hip"))
+    assert "hipGetLastError" in hip  # the scan sees the HIP imports at all
+    banned = [n for n in hip if re.match(r"hip(Malloc|Free|HostAlloc|HostMalloc|ExtMalloc|"
+                                         r"MallocAsync|MemPool|DeviceSynchronize|"
+                                         r"StreamSynchronize|EventSynchronize|Memcpy(?!ToSymbol))", n)]
+    assert banned == [], banned

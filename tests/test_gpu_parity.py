@@ -138,7 +138,9 @@ def test_invariants_on_device(d):
     q, k, v, _ = make_inputs(w, "cuda")
     ones = torch.ones_like(v)
     o, lse = gpu_fwd(q, k, ones, True, 0, w.scale)
-    assert np.abs(to64(o) - 1.0).max() <= 4e-3
+    # O is normalised by the sum of the same rounded weights the products use, so it is a
+    # convex combination of V rows: exactly 1 after the bf16 rounding
+    assert torch.equal(o, torch.ones_like(o))
     kz = torch.zeros_like(k)
     o, lse = gpu_fwd(q, kz, v, True, 0, w.scale)
     vv = to64(v)
@@ -197,8 +199,8 @@ def test_forward_is_deterministic_and_stream_ordered():
         dq2, dk2, dv2 = gpu_bwd(q, k, v, o1, do, l1, True, 0, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
-    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
-    assert (dq1.float() - dq2.float()).abs().max().item() <= 1e-2
+    # no atomics anywhere: every output is bitwise reproducible
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2) and torch.equal(dq1, dq2)
 
 
 def test_wrong_caller_buffers_are_rejected_before_launch():

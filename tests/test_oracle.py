@@ -13,7 +13,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (attention_probs, attention_probs_rows, attn_fwd_fp8, e4m3_decode, attn_bwd, attn_bwd_dkdv_cols, attn_bwd_dq_rows,
+from oracle import (attention_probs, attention_probs_rows, attn_fwd_fp8, e4m3_decode, attn_bwd,
+                    attn_bwd_dkdv_cols, attn_bwd_dkdv_cols_from_fwd, attn_bwd_dq_rows,
                     attn_bwd_head, attn_bwd_varlen, attn_fwd, attn_fwd_head, attn_fwd_rows,
                     attn_fwd_varlen, allowed_keys, attended_pairs)
 
@@ -282,6 +283,33 @@ def test_sampled_rows_match_full():
         dkc, dvc = attn_bwd_dkdv_cols(q, k, v, do, cols, causal, window, 0.3, row_chunk=37)
         np.testing.assert_allclose(dkc, dk[cols], atol=1e-12)
         np.testing.assert_allclose(dvc, dv[cols], atol=1e-12)
+
+
+@pytest.mark.parametrize("causal,window,slope", [(True, 0, 0.0), (True, 30, 0.0), (False, 0, 0.0),
+                                                 (False, 25, 0.0), (True, 0, 0.2),
+                                                 (False, 0, -0.1)])
+def test_dkdv_columns_from_forward_match_full_backward(causal, window, slope):
+    """dK/dV at selected keys from the forward's O and LSE equal the columns of the full
+    analytic backward (itself pinned by finite differences and torch's autograd), for every
+    mask, with a position bias, large logits, and row chunks that split the rows unevenly."""
+    rng = np.random.default_rng(31)
+    n, d = 230, 8
+    q, k, v, do = (_rand(rng, n, d) for _ in range(4))
+    q = 3.0 * q  # large logits: nearly one-hot rows
+    cols = np.array([0, 1, 31, 32, 100, 150, 228, 229])
+    o, lse = attn_fwd_head(q, k, v, causal, window, 0.3, slope=slope)
+    _, dk, dv, _ = attn_bwd_head(q, k, v, do, causal, window, 0.3, slope=slope)
+    dkc, dvc = attn_bwd_dkdv_cols_from_fwd(q, k, v, do, o, lse, cols, causal, window, 0.3,
+                                           row_chunk=41, slope=slope)
+    np.testing.assert_allclose(dkc, dk[cols], atol=1e-11, rtol=1e-10)
+    np.testing.assert_allclose(dvc, dv[cols], atol=1e-11, rtol=1e-10)
+    # a plausible slip (D taken from the wrong row, or P without its normaliser) is caught
+    dk_bad, _ = attn_bwd_dkdv_cols_from_fwd(q, k, v, do, np.roll(o, 1, axis=0), lse, cols,
+                                            causal, window, 0.3, slope=slope)
+    assert np.abs(dk_bad - dk[cols]).max() > 1e-3
+    _, dv_bad = attn_bwd_dkdv_cols_from_fwd(q, k, v, do, o, lse - 0.1, cols, causal, window,
+                                            0.3, slope=slope)
+    assert np.abs(dv_bad - dv[cols]).max() > 1e-3
 
 
 # ------------------------------------------------------------------ backward pins
