@@ -290,6 +290,28 @@ fa_status fa_bwd_alibi(const void* q, const void* k, const void* v, const void* 
                   window, scale, workspace, workspace_bytes, alibi_slopes, stream);
 }
 
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                         void* stream) {
+  static const char* fn = "fa_bwd_noalloc";
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_INVALID_ARG, "%s: null pointer", fn);
+  fa_status st = check_common(fn, B, Hq, Hkv, N, d, causal, window, scale);
+  if (st != FA_OK) return st;
+  if (sat_mul({B, Hq, N}) > (int64_t)fa::kNoAllocRows)
+    return fail(FA_ERR_WORKSPACE,
+                "%s: B*Hq*N = %lld rows exceed the %zu rows of its static workspace (use "
+                "fa_bwd with a caller workspace)", fn, (long long)B * Hq * N, fa::kNoAllocRows);
+  float* ws = nullptr;
+  const hipError_t e = fa::noalloc_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(FA_ERR_HIP, "%s: static workspace address: HIP error %d (%s)", fn, (int)e,
+                hipGetErrorString(e));
+  return bwd_bf16(fn, q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
+                  ws, fa::kNoAllocRows * sizeof(float), nullptr, stream);
+}
+
 fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
   if (!out) return fail(FA_ERR_INVALID_ARG, "fa_mfma_probe: null pointer");
   if (blocks <= 0 || iters <= 0)

@@ -28,10 +28,37 @@
 // the same shape as the forward: Q and dO rows are B operands in VGPRs, K, V and K^T tiles
 // stream through double-buffered LDS, and S^T / dP^T put one query row in each lane so LSE
 // and D are per-lane scalars and dS^T feeds dQ^T += K^T dS^T straight from the accumulator.
+#include <mutex>
+
 #include "fa_common.hpp"
 #include "fa_kernels.hpp"
 
 namespace fa {
+
+// Workspace of the no-allocation backward (fa_bwd_noalloc): the D vector of up to
+// kNoAllocRows rows in a static device array.  Every device the library runs on holds its
+// own copy for the life of the process; in host code only the address that
+// hipGetSymbolAddress returns for the current device may be used, never the array's name.
+__device__ __align__(256) float scratch[kNoAllocRows];
+
+hipError_t noalloc_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static float* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<float*>(p);
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
+}
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -63,6 +63,11 @@ struct DecodeArgs {
   hipEvent_t ev_stop;
 };
 
+// Rows of float32 D the no-allocation backward's static workspace holds (16 MiB).
+constexpr size_t kNoAllocRows = (size_t)1 << 22;
+// Device address of that workspace on the current device (resolved once per device).
+hipError_t noalloc_scratch(float** ptr);
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_fwd_fp32(const FwdArgs& a, hipStream_t st);

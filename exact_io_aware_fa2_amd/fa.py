@@ -24,7 +24,8 @@ FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = ra
 
 EXPORTED = ("fa_fwd", "fa_fwd_alibi", "fa_fwd_fp32", "fa_fwd_fp8", "fa_decode",
             "fa_decode_num_splits", "fa_decode_workspace_size", "fa_bwd", "fa_bwd_alibi",
-            "fa_bwd_workspace_size", "fa_fwd_varlen", "fa_fwd_varlen_alibi", "fa_bwd_varlen",
+            "fa_bwd_noalloc", "fa_bwd_workspace_size", "fa_fwd_varlen", "fa_fwd_varlen_alibi",
+            "fa_bwd_varlen",
             "fa_bwd_varlen_alibi", "fa_bwd_varlen_workspace_size", "fa_bwd_time_main_kernel",
             "fa_mfma_probe", "fa_last_error", "fa_version")
 
@@ -64,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.fa_bwd_alibi.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp,
                                  sz, vp, vp]
     lib.fa_bwd_alibi.restype = i
+    lib.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.fa_bwd_noalloc.restype = i
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_varlen.restype = i
     lib.fa_fwd_varlen_alibi.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, vp]
@@ -157,6 +160,13 @@ def fa_bwd_alibi(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, wind
                                _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal),
                                int(window), float(scale), _ptr(workspace),
                                int(workspace_bytes), _ptr(alibi_slopes), _stream(stream))
+
+
+def fa_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, B, Hq, Hkv, N, d, causal, window, scale,
+                   stream=None) -> int:
+    return load().fa_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal),
+                                 int(window), float(scale), _stream(stream))
 
 
 def fa_fwd_varlen(q, k, v, o, lse, cu_seqlens, num_seqs, total, max_seqlen, Hq, Hkv, d, causal,

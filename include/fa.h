@@ -156,6 +156,22 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  int N, int d, int causal, int window, float scale, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * D = rowsum(dO * O) goes to a static device array of the library instead: 16 MiB per GPU
+ * (B * Hq * N <= 4194304 rows of float32), held by every GPU the library runs on until the
+ * process ends.  The call allocates nothing.  Larger sizes return FA_ERR_WORKSPACE.  All
+ * calls on one GPU share that array and each overwrites it completely before reading it:
+ * calls that overlap on one GPU (different streams or threads without ordering between
+ * them) race and give wrong gradients.  Results are bitwise those of fa_bwd.  Other rules
+ * as fa_bwd.
+ */
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,
+                         int Hq, int Hkv, int N, int d, int causal, int window, float scale,
+                         void* stream);
+
 /* fa_bwd for the forward of fa_fwd_alibi (the same slopes); NULL slopes are rejected. */
 fa_status fa_bwd_alibi(const void* q, const void* k, const void* v, const void* o,
                        const void* dO, const float* lse, void* dq, void* dk, void* dv, int B,

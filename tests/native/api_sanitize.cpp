@@ -68,6 +68,14 @@ int main() {
                      nullptr) == FA_OK);
   CHECK(stub::calls_bwd == 2 && stub::bwd.slopes == F);
 
+  // no-allocation backward: the static workspace stands in for the caller's
+  CHECK(fa_bwd_noalloc(A, A, A, A, A, F, A, A, A, 2, 8, 2, 300, 128, 1, 0, 0.1f, nullptr) ==
+        FA_OK);
+  CHECK(stub::calls_bwd == 3 && stub::bwd.dvec != nullptr && stub::bwd.dvec != F);
+  CHECK(stub::bwd.slopes == nullptr && stub::bwd.N == 300);
+  CHECK(fa_bwd_noalloc(A, A, A, A, A, F, A, A, A, 1, 64, 8, 65536, 128, 1, 0, 0.1f, nullptr) ==
+        FA_OK);  // 2^22 rows: exactly the limit
+
   // packed sequences
   CHECK(fa_fwd_varlen(A, A, A, A, F, I, 3, 64, 40, 4, 2, 128, 1, 0, 0.1f, nullptr) == FA_OK);
   CHECK(stub::fwd.cu == I && stub::fwd.ntot == 64 && stub::fwd.N == 40 && stub::fwd.B == 3);
@@ -110,6 +118,10 @@ int main() {
                nullptr) == FA_ERR_INVALID_ARG);
   CHECK(fa_fwd_alibi(A, A, A, A, F, 1, 2, 2, 16, 64, 0, 0, 0.1f, nullptr, nullptr) ==
         FA_ERR_INVALID_ARG);
+  CHECK(fa_bwd_noalloc(A, A, A, A, A, F, A, A, A, 1, 64, 8, 65537, 64, 1, 0, 0.1f, nullptr) ==
+        FA_ERR_WORKSPACE);  // one row past the static workspace
+  CHECK(fa_bwd_noalloc(A, A, A, A, nullptr, F, A, A, A, 1, 4, 2, 64, 64, 1, 0, 0.1f,
+                       nullptr) == FA_ERR_INVALID_ARG);
   CHECK(fa_bwd(A, A, A, A, A, F, A, A, A, 2, 8, 2, 300, 128, 1, 0, 0.1f, A, need - 1,
                nullptr) == FA_ERR_WORKSPACE);
   CHECK(fa_bwd(A, A, A, A, A, F, A, A, A, 2, 8, 2, 300, 128, 1, 0, 0.1f, (char*)A + 128, need,
