@@ -215,3 +215,30 @@ def test_wrong_caller_buffers_are_rejected_before_launch():
         fa.backward(q, k, v, o, do, lse, causal=True, dq=torch.empty_like(q, dtype=torch.float32))
     with pytest.raises(ValueError, match="one dtype"):
         fa.forward(q, k.float(), v, causal=True)
+
+
+def test_forward_and_backward_allocate_no_device_memory():
+    """O(N) memory (ainews.cool "flash-attention transformer optimization", technical deep
+    dive, memory table): with the caller's buffers in place, repeated forward and backward
+    calls leave the device's free memory exactly where it was: no N x N matrix, and no
+    hidden allocation of any size."""
+    from exact_io_aware_fa2_amd import fa
+    w = _case((2, 8, 2, 4096, 128, True, 0), seed=14)
+    q, k, v, do = make_inputs(w, "cuda")
+    o, lse = torch.empty_like(q), torch.empty((2, 8, 4096), device="cuda", dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = fa.workspace_for(2, 8, 2, 4096, 128, True, 0, q.device)
+    assert ws.numel() == 2 * 8 * 4096 * 4  # D only: linear in N
+
+    def step():
+        assert fa.fa_fwd(q, k, v, o, lse, 2, 8, 2, 4096, 128, 1, 0, w.scale) == fa.FA_OK
+        assert fa.fa_bwd(q, k, v, o, do, lse, dq, dk, dv, 2, 8, 2, 4096, 128, 1, 0, w.scale, ws,
+                         ws.numel()) == fa.FA_OK
+
+    step()  # first launches load the code objects
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    assert torch.cuda.mem_get_info()[0] == free0
