@@ -34,6 +34,16 @@ typedef __attribute__((address_space(3))) char lds_char;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Lazy reference maximum of the forward kernels.  A piece whose weights against the
+// current reference would exceed kSumLimit = 2^12 (detected from a lane's partial sum, so
+// the common path takes no row max at all) goes through the rescale path, which moves the
+// reference only for rows whose piece maximum exceeds it by more than kRescaleThreshold
+// log2 units.  Weights thus stay below 2^12 and the accumulator rescale (a multiply of
+// every accumulator register) runs rarely.  Numerator and denominator always share the same
+// reference maximum, so the normalised result is unchanged.
+constexpr float kRescaleThreshold = 8.f;
+constexpr float kSumLimit = 4096.f;
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

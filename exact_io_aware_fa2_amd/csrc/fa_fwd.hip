@@ -41,16 +41,6 @@ struct FwdCfg {
   static constexpr int LDS_BYTES = 2 * BUF_ELEMS * 2;  // double buffered
 };
 
-// Lazy reference maximum.  A piece whose weights against the current reference would
-// exceed kSumLimit = 2^12 (detected from a lane's partial sum, so the common path takes no
-// row max at all) goes through the rescale path, which moves the reference only for rows
-// whose piece maximum exceeds it by more than kRescaleThreshold log2 units.  Weights thus
-// stay below 2^12 and the accumulator rescale (a multiply of every accumulator register)
-// runs rarely.  Numerator and denominator always share the same reference maximum, so the
-// normalised result is unchanged.
-constexpr float kRescaleThreshold = 8.f;
-constexpr float kSumLimit = 4096.f;
-
 __device__ __forceinline__ uint32_t word(const uint4& u, int m) {
   return m == 0 ? u.x : m == 1 ? u.y : m == 2 ? u.z : u.w;
 }
@@ -115,77 +105,116 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   if (window > 0) kv_lo = max(0, m0 - window + 1);
   const int nb_lo = kv_lo / BN, nb_hi = (kv_hi + BN - 1) / BN;
 
-  // Staging: K rows as 16-byte chunks; V as 4 keys x 8 dims per task, transposed in
-  // registers (16-bit lane packing) and stored as V^T rows.
+  // Staging.  d <= 128 (64-key tiles, 512 threads): thread = (key pair kp, 8-dim chunk dcp)
+  // of K and of V, K stored row-major and V transposed (16-bit lane packing, one 32-bit
+  // word per V^T row), the same work for every thread; key pairs run fastest inside a
+  // wave, which keeps both kinds of store free of bank conflicts.  d = 256 (32-key tiles,
+  // 256 threads): K rows as 16-byte chunks, V as 4 keys x 8 dims per task, transposed in
+  // registers.  Tiles are read through buffer resources whose size ends at row N, so rows
+  // past the end of the sequence load as zeros.
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-  constexpr int KCH = BN * CPR;           // K chunks per tile
-  constexpr int PTK = (KCH + NT - 1) / NT;
-  constexpr int VTASKS = (BN / 4) * CPR;  // (4-key group, 8-dim chunk) tasks
+  constexpr bool kPairs = D <= 128;
+  constexpr int TP = (BN / 2) * CPR;      // key-pair tasks per tile (d <= 128)
+  static_assert(!kPairs || TP <= NT, "one key-pair task per thread");
+  constexpr int KCH = BN * CPR;           // K chunks per tile (d = 256)
+  constexpr int PTK = kPairs ? 1 : (KCH + NT - 1) / NT;
+  constexpr int VTASKS = (BN / 4) * CPR;  // (4-key group, 8-dim chunk) tasks (d = 256)
   static_assert(BN % 16 == 0, "task_rc needs whole groups of 16 keys");
-  constexpr int PTV = (VTASKS + NT - 1) / NT;
-  // Tiles are read through buffer resources whose size ends at row N, so rows past the end
-  // of the sequence load as zeros; the per-thread byte offsets inside a tile are fixed.
+  constexpr int PTV = kPairs ? 1 : (VTASKS + NT - 1) / NT;
+  const uint32_t row_bytes = (uint32_t)ks * 2u;
+  // d <= 128
+  const bool ptask = TP == NT || tid < TP;
+  const int kp = tid % (BN / 2), dcp = tid / (BN / 2);
+  const uint32_t poff = (uint32_t)(2 * kp * ks + 8 * dcp) * 2u;
+  uint4 xk[2], xv[2];
+  // d = 256
   uint4 kr[PTK], vr[PTV][4];
   uint32_t koff[PTK], voff[PTV];
+  if constexpr (!kPairs) {
 #pragma unroll
-  for (int i = 0; i < PTK; ++i) {
-    const int ch = tid + NT * i;
-    const int key = ch / CPR, dc = ch - key * CPR;
-    koff[i] = (uint32_t)(key * ks + dc * 8) * 2u;
-  }
+    for (int i = 0; i < PTK; ++i) {
+      const int ch = tid + NT * i;
+      const int key = ch / CPR, dc = ch - key * CPR;
+      koff[i] = (uint32_t)(key * ks + dc * 8) * 2u;
+    }
 #pragma unroll
-  for (int p = 0; p < PTV; ++p) {
-    int kg, dc;
-    task_rc<CPR>(tid + NT * p, kg, dc);
-    voff[p] = (uint32_t)(4 * kg * ks + dc * 8) * 2u;
+    for (int p = 0; p < PTV; ++p) {
+      int kg, dc;
+      task_rc<CPR>(tid + NT * p, kg, dc);
+      voff[p] = (uint32_t)(4 * kg * ks + dc * 8) * 2u;
+    }
   }
-  const uint32_t row_bytes = (uint32_t)ks * 2u;
   auto gload = [&](int nb) {
     const int n0 = nb * BN;
     const uint32_t bytes = (uint32_t)(N - n0) * row_bytes;
     const rsrc_t kres = make_rsrc(Kh + (size_t)n0 * ks, bytes);
     const rsrc_t vres = make_rsrc(Vh + (size_t)n0 * ks, bytes);
+    if constexpr (kPairs) {
+      if (ptask) {
+        xk[0] = bload16(kres, poff);
+        xk[1] = bload16(kres, poff + row_bytes);
+        xv[0] = bload16(vres, poff);
+        xv[1] = bload16(vres, poff + row_bytes);
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < PTK; ++i) {
-      if (KCH % NT == 0 || tid + NT * i < KCH) kr[i] = bload16(kres, koff[i]);
-    }
+      for (int i = 0; i < PTK; ++i) {
+        if (KCH % NT == 0 || tid + NT * i < KCH) kr[i] = bload16(kres, koff[i]);
+      }
 #pragma unroll
-    for (int p = 0; p < PTV; ++p) {
-      if (VTASKS % NT == 0 || tid + NT * p < VTASKS) {
+      for (int p = 0; p < PTV; ++p) {
+        if (VTASKS % NT == 0 || tid + NT * p < VTASKS) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[p][e] = bload16(vres, voff[p] + e * row_bytes);
+          for (int e = 0; e < 4; ++e) vr[p][e] = bload16(vres, voff[p] + e * row_bytes);
+        }
       }
     }
   };
   auto swrite = [&](int buf) {
     bf16_t* sK = lds + buf * Cfg::BUF_ELEMS;
     bf16_t* sV = sK + Cfg::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < PTK; ++i) {
-      const int ch = tid + NT * i;
-      if (KCH % NT == 0 || ch < KCH) {
-        const int key = ch / CPR, dc = ch - key * CPR;
-        *reinterpret_cast<uint4*>(sK + key * KSTR + dc * 8) = kr[i];
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < PTV; ++p) {
-      const int task = tid + NT * p;
-      if (VTASKS % NT == 0 || task < VTASKS) {
-        int kg, dc;
-        task_rc<CPR>(task, kg, dc);
-        bf16_t* dst = sV + (dc * 8) * VSTR + vt_pos(4 * kg);
+    if constexpr (kPairs) {
+      if (ptask) {
+        bf16_t* kd = sK + (2 * kp) * KSTR + 8 * dcp;
+        *reinterpret_cast<uint4*>(kd) = xk[0];
+        *reinterpret_cast<uint4*>(kd + KSTR) = xk[1];
+        // dim 8 dcp + j of the two keys -> one 32-bit word of V^T row 8 dcp + j
+        bf16_t* vd = sV + (8 * dcp) * VSTR + vt_pos(2 * kp);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const uint32_t a0 = word(vr[p][0], m), a1 = word(vr[p][1], m);
-          const uint32_t a2 = word(vr[p][2], m), a3 = word(vr[p][3], m);
-          uint2 even, odd;  // dims 2m and 2m+1, keys 0..3 of the group
-          even.x = pack_lo(a0, a1);
-          even.y = pack_lo(a2, a3);
-          odd.x = pack_hi(a0, a1);
-          odd.y = pack_hi(a2, a3);
-          *reinterpret_cast<uint2*>(dst + (2 * m) * VSTR) = even;
-          *reinterpret_cast<uint2*>(dst + (2 * m + 1) * VSTR) = odd;
+          const uint32_t a0 = word(xv[0], m), a1 = word(xv[1], m);
+          *reinterpret_cast<uint32_t*>(vd + (2 * m) * VSTR) = pack_lo(a0, a1);
+          *reinterpret_cast<uint32_t*>(vd + (2 * m + 1) * VSTR) = pack_hi(a0, a1);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PTK; ++i) {
+        const int ch = tid + NT * i;
+        if (KCH % NT == 0 || ch < KCH) {
+          const int key = ch / CPR, dc = ch - key * CPR;
+          *reinterpret_cast<uint4*>(sK + key * KSTR + dc * 8) = kr[i];
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < PTV; ++p) {
+        const int task = tid + NT * p;
+        if (VTASKS % NT == 0 || task < VTASKS) {
+          int kg, dc;
+          task_rc<CPR>(task, kg, dc);
+          bf16_t* dst = sV + (dc * 8) * VSTR + vt_pos(4 * kg);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t a0 = word(vr[p][0], m), a1 = word(vr[p][1], m);
+            const uint32_t a2 = word(vr[p][2], m), a3 = word(vr[p][3], m);
+            uint2 even, odd;  // dims 2m and 2m+1, keys 0..3 of the group
+            even.x = pack_lo(a0, a1);
+            even.y = pack_lo(a2, a3);
+            odd.x = pack_hi(a0, a1);
+            odd.y = pack_hi(a2, a3);
+            *reinterpret_cast<uint2*>(dst + (2 * m) * VSTR) = even;
+            *reinterpret_cast<uint2*>(dst + (2 * m + 1) * VSTR) = odd;
+          }
         }
       }
     }
