@@ -98,6 +98,43 @@ def mfma_probe(fa, torch, dev, stream, blocks: int = 2048, iters: int = 20000, r
     return flop / (best * 1e-3) / 1e12
 
 
+def atomic_dq_count(w, bkn: int = 256, bq: int = 32) -> int:
+    """float32 atomic adds an atomic accumulation of dQ would issue for a fixed-length
+    workload: every key block of `bkn` keys adds, for each 32-row step it visits (the same
+    steps the key-block kernel walks) and each query head of its group, one 32 x d tile of
+    its contribution summed over its keys."""
+    total = 0
+    for kb in range((w.N + bkn - 1) // bkn):
+        n0 = kb * bkn
+        qb_lo = n0 // bq if w.causal else 0
+        row_end = min(w.N, n0 + bkn + w.window - 1) if w.window > 0 else w.N
+        total += max(0, (row_end + bq - 1) // bq - qb_lo)
+    return total * w.B * w.Hq * bq * w.d
+
+
+def atomic_probe(fa, torch, dev, stream, w, blocks: int = 2048, iters: int = 64):
+    """Measured float32 atomic rate (adds/s) in the tile pattern of an atomic dQ, into an
+    accumulator of the workload's [B, N, Hq, d] shape (best of 3)."""
+    stride = w.Hq * w.d
+    row_blocks = (w.B * w.N) // 32
+    acc = torch.zeros(row_blocks * 32 * stride, dtype=torch.float32, device=dev)
+    sh = stream.cuda_stream
+    if fa.fa_atomic_probe(acc, row_blocks, stride, blocks, 4, sh) != fa.FA_OK:
+        raise RuntimeError(fa.fa_last_error())
+    best = None
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        if fa.fa_atomic_probe(acc, row_blocks, stride, blocks, iters, sh) != fa.FA_OK:
+            raise RuntimeError(fa.fa_last_error())
+        e1.record(stream)
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del acc
+    return blocks * iters * 4096 / (best * 1e-3), best
+
+
 def _head_tasks(w, q, k, v, do, packed):
     """(flop, task maker) per (batch entry or sequence, query head), in an order that
     spreads a prefix over every sequence length: head-major for packed batches."""
@@ -169,10 +206,12 @@ def cpu_baseline(w, q, k, v, do, packed=False, max_workers: int = 16):
         "value": flop / dt / 1e12,
         "unit": "TFLOP/s (fwd+bwd, algorithmic)" if bwd else "TFLOP/s (fwd, algorithmic)",
         "cores": workers,
+        "host_cores": cores,
         "kind": "oracle",
         "sample": f"{len(tasks)} of {n_all} {what} pairs of {w.name}, "
                   f"{'forward + backward' if bwd else 'forward'}, float64 NumPy, "
-                  f"{workers} worker processes x 1 BLAS thread, {dt:.1f} s wall",
+                  f"{workers} worker processes x 1 BLAS thread on a host with {cores} "
+                  f"cores, {dt:.1f} s wall",
         "seconds": dt,
     }
 
@@ -209,6 +248,7 @@ def cpu_baseline_decode(w, q, k, v, flop_per_seq, max_workers: int = 16):
         "value": sum(flop_per_seq) / dt / 1e12,
         "unit": "TFLOP/s (decode, algorithmic)",
         "cores": workers,
+        "host_cores": cores,
         "kind": "oracle",
         "sample": f"all {w.B} sequences of {w.name}, float64 NumPy attn_decode, {workers} worker "
                   f"processes x 1 BLAS thread, {dt:.1f} s wall",
@@ -326,6 +366,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the products-only MFMA throughput probe (profiling runs)")
+    ap.add_argument("--probe-atomic-dq", action="store_true",
+                    help="also time float32 atomics in the pattern of an atomic dQ and price "
+                         "that alternative to the separate dQ pass at this workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -486,12 +529,15 @@ def main() -> int:
         out["bwd_dq_kernel_ms"] = avg(q_ms)
         out["fwd_bwd_tflops_kernels"] = total_flop / ((fwd_avg + avg(bwd_ms)) * 1e-3) / 1e12
         out["fwd_bwd_frac_of_peak"] = out["value"] / MFMA_BF16_PEAK_TFLOPS
-        # algorithmic products executed by each kernel: dK/dV kernel S, dP, dV, dK (4 per
-        # pair, 2x the forward); dQ kernel S, dP, dQ (3 per pair, 1.5x the forward)
-        # d <= 128 runs the 8-wave key-block kernel, d = 256 the 4-wave one
+        # Algorithmic work of each kernel (its share of the five products per attended pair,
+        # 2.5x the forward): the dK/dV kernel does S, dP, dV and dK (2x the forward); the dQ
+        # kernel's own product is dQ (0.5x the forward) -- it also recomputes S and dP, which
+        # is work of the method's two-kernel schedule, not of the algorithm, and earns no
+        # credit here.  d <= 128 runs the 8-wave key-block kernel, d = 256 the 4-wave one.
         kv_name = "bwd_dkdv8_kernel" if w.d <= 128 else "bwd_dkdv_kernel"
         kernels[kv_name] = (avg(kv_ms), 2.0 * F, "fa_bwd.hip")
-        kernels["bwd_dq_kernel"] = (avg(q_ms), 1.5 * F, "fa_bwd.hip")
+        kernels["bwd_dq_kernel"] = (avg(q_ms), 0.5 * F, "fa_bwd.hip")
+        out["bwd_dq_kernel_executed_tflops"] = 1.5 * F / (avg(q_ms) * 1e-3) / 1e12
     med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
     stats = {"fwd": fwd_ms}
     if bwd:
@@ -520,6 +566,17 @@ def main() -> int:
             "frac_of_measured_mfma": achieved / probe if probe else None,
         }
         out["fwd_frac_of_measured_mfma"] = out["fwd_tflops"] / probe if probe else None
+    if args.probe_atomic_dq and bwd and not packed:
+        rate, ms = atomic_probe(fa, torch, dev, stream, w)
+        need = atomic_dq_count(w)
+        out["atomic_dq"] = {
+            "probe_atomics_per_s": rate, "probe_ms": ms,
+            "atomics_for_workload": need,
+            "atomic_adds_ms_estimate": need / rate * 1e3,
+            "separate_dq_pass_ms": out["bwd_dq_kernel_ms"],
+            "note": "time of the atomic adds alone, at the probe's rate; an atomic dQ would "
+                    "also add the dQ products and a transpose of dS to the key-block kernel, "
+                    "and a zeroing and a conversion pass of the float32 accumulator"}
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

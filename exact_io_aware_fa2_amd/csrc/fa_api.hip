@@ -319,6 +319,18 @@ fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream) {
   return launched("fa_mfma_probe", fa::launch_mfma_probe(out, blocks, iters, (hipStream_t)stream));
 }
 
+fa_status fa_atomic_probe(float* acc, int row_blocks, int stride, int blocks, int iters,
+                          void* stream) {
+  if (!acc) return fail(FA_ERR_INVALID_ARG, "fa_atomic_probe: null pointer");
+  if (row_blocks <= 0 || stride < 128 || blocks <= 0 || iters <= 0)
+    return fail(FA_ERR_INVALID_ARG,
+                "fa_atomic_probe: row_blocks, blocks and iters must be positive, stride >= 128");
+  if (sat_mul({row_blocks, 32, stride}) >= kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "fa_atomic_probe: row_blocks * 32 * stride reaches 2^31");
+  return launched("fa_atomic_probe", fa::launch_atomic_probe(acc, row_blocks, stride, blocks,
+                                                             iters, (hipStream_t)stream));
+}
+
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
                         int Hkv, int d, int causal, int window, float scale, void* stream) {

@@ -277,6 +277,20 @@ fa_status fa_bwd_time_main_kernel(void* start_event, void* stop_event);
  */
 fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream);
 
+/*
+ * Measurement aid (no counterpart on the pages): price the atomic alternative to the
+ * separate dQ pass.  Enqueues `blocks` workgroups of 256 threads; each adds, `iters` times,
+ * a 32 x 128 tile of float32 values (1/1024 each) with global float atomics into the
+ * caller-owned accumulator `acc` of row_blocks * 32 rows whose rows are `stride` floats
+ * apart, visiting row blocks in a pseudo-random order.  The adds follow the layout of a
+ * 32 x 32 MFMA accumulator: each wave-wide atomic covers two rows of 32 consecutive floats.  So blocks * iters * 4096 atomic
+ * adds are issued; their rate is that count over the elapsed time.  `acc` must hold
+ * row_blocks * 32 * stride floats; its contents change.  FA_ERR_INVALID_ARG for a null
+ * pointer, non-positive counts, stride < 128 or row_blocks * 32 * stride >= 2^31.
+ */
+fa_status fa_atomic_probe(float* acc, int row_blocks, int stride, int blocks, int iters,
+                          void* stream);
+
 /* Message for the last non-FA_OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);
 

@@ -112,6 +112,16 @@ def test_mfma_probe_validation():
     assert fa.fa_mfma_probe(1 << 20, 4, -1, stream=0) == fa.FA_ERR_INVALID_ARG
 
 
+def test_atomic_probe_validation():
+    assert fa.fa_atomic_probe(None, 8, 4096, 4, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_atomic_probe(1 << 20, 0, 4096, 4, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_atomic_probe(1 << 20, 8, 64, 4, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_atomic_probe(1 << 20, 8, 4096, 4, 0, stream=0) == fa.FA_ERR_INVALID_ARG
+    # 2^31 floats would not be addressable with the kernel's 32-bit row arithmetic
+    assert fa.fa_atomic_probe(1 << 20, 1 << 14, 4096, 4, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert "2^31" in fa.fa_last_error()
+
+
 BAD_VARLEN = [
     (dict(cu=None), fa.FA_ERR_INVALID_ARG),
     (dict(num_seqs=0), fa.FA_ERR_INVALID_ARG),
