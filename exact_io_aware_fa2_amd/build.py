@@ -35,9 +35,17 @@ HIPCC_FLAGS = [
 # Per-source flags.  The two forward kernels measured 1-3 % faster (interleaved A/B runs)
 # with the backend's iterative register-minimising scheduler; the backward kernels are
 # fastest with the default one.
+# VGPR-form matrix products: a kernel that needs more than 256 registers per lane (the
+# head-dim-256 instances, one wave per SIMD) otherwise gets its products in the AGPR form,
+# and the backend then moves accumulators and operands between AGPRs and VGPRs around every
+# product and every softmax (hundreds of v_accvgpr moves per 32-key piece).  With the VGPR
+# form the accumulators stay in VGPRs and AGPRs only hold values spilled out of the loop's
+# way.  Kernels within 256 registers compile to identical code either way.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 FILE_FLAGS = {
-    "fa_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
-    "fa_fwd_fp8.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
+    "fa_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"] + VGPR_FORM,
+    "fa_fwd_fp8.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"] + VGPR_FORM,
+    "fa_bwd.hip": VGPR_FORM,
 }
 
 

@@ -1,9 +1,12 @@
 """Build checks on the CPU (hipcc cross-compiles for gfx950 without a GPU).
 
-The kernels for head dims 64 and 128 must compile without vector-register spills: a spill
-to scratch memory inside their inner loops costs more than the changes that would cause one
-save.  The check uses
-the flags of the real build (exact_io_aware_fa2_amd/build.py, per-source flags included).
+No kernel may use scratch memory (register spills to memory inside an inner loop cost more
+than the changes that would cause one save).  The kernels for head dims 64 and 128 must
+also compile without any vector-register spill; the head-dim-256 kernels run one wave per
+SIMD with up to 512 registers per lane, where a few values parked in AGPRs (counted as
+spills by the compiler, but register moves, not memory traffic) are allowed.  The check
+uses the flags of the real build (exact_io_aware_fa2_amd/build.py, per-source flags
+included).
 """
 
 import concurrent.futures
@@ -33,7 +36,8 @@ def _resource_usage(src: str, tmpdir: str) -> dict:
             name = m.group(1)
             usage[name] = {}
             continue
-        m = re.search(r"remark:\s+(VGPRs|AGPRs|VGPRs Spill|SGPRs Spill): (\d+)", line)
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|VGPRs Spill|SGPRs Spill|ScratchSize) ?"
+                      r"(?:\[bytes/lane\])?: (\d+)", line)
         if m and name:
             usage[name][m.group(1)] = int(m.group(2))
     return usage
@@ -64,3 +68,17 @@ def test_no_vector_register_spills_for_head_dims_up_to_128(usage):
     bad = {n: u for n, u in usage.items()
            if ("ILi64E" in n or "ILi128E" in n) and u.get("VGPRs Spill", 0) > 0}
     assert not bad, bad
+
+
+def test_no_kernel_uses_scratch_memory(usage):
+    assert usage, "no kernels reported"
+    missing = [n for n, u in usage.items() if "ScratchSize" not in u]
+    assert not missing, missing
+    bad = {n: u for n, u in usage.items() if u["ScratchSize"] > 0}
+    assert not bad, bad
+
+
+def test_head_dim_256_kernels_are_covered(usage):
+    names = " ".join(n for n in usage if "ILi256E" in n)
+    for k in ("fwd_bf16_kernel", "fwd_fp8_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
+        assert k in names, k
