@@ -180,8 +180,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   const int qb_hi = (row_end + BQ - 1) / BQ;
   const int nq = max(0, qb_hi - qb_lo);
   const int total_it = G * nq;
+  // Step it = (query block qi, query head g of the group) = (it / G, it % G): query-block
+  // major, so the workgroups of one KV head that run together read the same Q / dO rows
+  // at about the same time and share them in L2.  Causal blocks walk their query blocks
+  // from the last one down: all start at the end of the sequence and stop at their own
+  // diagonal, instead of each starting at a different row.
+  auto qblock = [&](int qi) { return causal ? qb_hi - 1 - qi : qb_lo + qi; };
   // ALiBi slope (log2 units) of the query head of step it
-  auto slope_of = [&](int it) { return AL != 0 ? slopes[hkv * G + it / nq] * kLog2e : 0.f; };
+  auto slope_of = [&](int it) { return AL != 0 ? slopes[hkv * G + it % G] * kLog2e : 0.f; };
 
   f32x16 dk[NDH], dv[NDH];
 #pragma unroll
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   uint4 qr[PT][4], orr[PT][4];
   float lreg = 0.f, dreg = 0.f;
   auto gload = [&](int it) {
-    const int g = it / nq, qb = qb_lo + (it - g * nq);
+    const int qi = it / G, g = it - qi * G, qb = qblock(qi);
     const int hq = hkv * G + g, r0 = qb * BQ;
     const bf16_t* Qb = Q + ((size_t)seq0 * Hq + hq) * D;
     const bf16_t* Ob = dO + ((size_t)seq0 * Hq + hq) * D;
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const bf16_t* sOT = sQT + Cfg::SQT;
     const float* sL = reinterpret_cast<const float*>(sOT + Cfg::SQT);
     const float* sD = sL + BQ;
-    const int g = it / nq, qb = qb_lo + (it - g * nq);
+    const int qi = it / G, g = it - qi * G, qb = qblock(qi);
     const int r0 = qb * BQ;
     (void)g;
     const bool active = kw0 < N && (!causal || r0 + BQ - 1 >= kw0) &&
@@ -470,12 +476,17 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   const int qb_hi = (row_end + BQ - 1) / BQ;
   const int nq = max(0, qb_hi - qb_lo);
   const int total_it = G * nq;
-  // A step is (query head g of the group, query block qb_lo + qi), g-major.  Steps advance
-  // by counting, not by dividing the step index by nq (a scalar division per use).
+  // A step is (query block qi, query head g of the group), query-block major, so the
+  // workgroups of one KV head that run together read the same Q / dO rows at about the same
+  // time and share them in L2.  Causal blocks walk their query blocks from the last one
+  // down: all start at the end of the sequence and stop at their own diagonal, instead of
+  // each starting at a different row.  Steps advance by counting, not by dividing the step
+  // index (a scalar division per use).
   struct Step {
     int g, qi;
   };
-  auto adv = [&](Step st) { return st.qi + 1 == nq ? Step{st.g + 1, 0} : Step{st.g, st.qi + 1}; };
+  auto adv = [&](Step st) { return st.g + 1 == G ? Step{0, st.qi + 1} : Step{st.g + 1, st.qi}; };
+  auto qblock = [&](int qi) { return causal ? qb_hi - 1 - qi : qb_lo + qi; };
   // ALiBi slope (log2 units) of query head g of the group
   auto slope_of = [&](int g) { return AL != 0 ? slopes[hkv * G + g] * kLog2e : 0.f; };
 
@@ -505,7 +516,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   uint4 xr[2];
   float lraw = 0.f, draw = 0.f;
   auto gload = [&](Step st) {
-    const int hq = hkv * G + st.g, r0 = (qb_lo + st.qi) * BQ;
+    const int hq = hkv * G + st.g, r0 = qblock(st.qi) * BQ;
     if (stager) {
       const bf16_t* base = (iso ? dO : Q) + ((size_t)seq0 * Hq + hq) * D + (size_t)r0 * qs;
       const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
@@ -542,7 +553,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
       }
     }
     if (tid < BQ) {
-      const bool in = (qb_lo + st.qi) * BQ + tid < N;
+      const bool in = qblock(st.qi) * BQ + tid < N;
       // +inf -> P = 0 on padding rows.  Causal position bias: LSE + slope2 (row - r0) is
       // staged and slope2 (key - r0) added per lane, both small near the diagonal.
       sL[tid] = in ? lraw * kLog2e + (AL == 1 ? slope_of(st.g) * tid : 0.f) : INFINITY;
@@ -567,7 +578,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
     const bf16_t* sOT = sQT + Cfg::SQT;
     const float* sL = reinterpret_cast<const float*>(sOT + Cfg::SQT);
     const float* sD = sL + BQ;
-    const int r0 = (qb_lo + cur.qi) * BQ;
+    const int r0 = qblock(cur.qi) * BQ;
     const bool active = kw0 < N && (!causal || r0 + BQ - 1 >= kw0) &&
                         (window <= 0 || r0 <= kw0 + 31 + window - 1);
     if (active) {

@@ -60,6 +60,8 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   constexpr int NT = Cfg::NT, BM = Cfg::BM, BN = Cfg::BN, KSTR = Cfg::KSTR, VSTR = Cfg::VSTR;
   constexpr int NC = D / 16;  // k-steps of S^T over the head dim
   constexpr int ND = D / 32;  // 32-wide head-dim tiles of O^T
+  constexpr bool kStream = D > 128;   // K / V^T operands streamed (see the piece loop)
+  constexpr int kRing = 4, kAhead = 3;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
 
@@ -274,25 +276,44 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
         const int k0 = n0 + 32 * kt;
         if (causal && k0 > wr0 + 31) break;  // this half is entirely above the diagonal
         // S^T tile: keys k0 + [0, 32) x this wave's 32 rows.
-        // All K operands of the piece are read before the MFMAs that use them, and the V^T
-        // operands right after, so LDS latency hides behind the MFMAs and the softmax.
+        // d <= 128: all K operands of the piece are read before the MFMAs that use them, and
+        // the V^T operands right after, so LDS latency hides behind the MFMAs and the softmax.
         const bf16_t* kp = sK + (32 * kt + l32) * KSTR + 8 * hh;
-        bf16x8 kop[NC];
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) kop[cc] = lds_read_b128(kp + 16 * cc);
-        f32x16 s = zero16();
-        // Raised wave priority over each MFMA run: the other wave on the SIMD gets the
-        // softmax VALU slots while this one keeps the matrix core fed.
-        __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) s = mfma32(kop[cc], qop[cc], s);
-        __builtin_amdgcn_s_setprio(0);
         const bf16_t* vp = sV + l32 * VSTR + 8 * hh + 32 * kt;
-        bf16x8 vop[ND][2];
+        // V^T operand j = 2 dt + c2 (head-dim tile dt, key half c2)
+        auto vread = [&](int j) { return lds_read_b128(vp + 32 * (j >> 1) * VSTR + 16 * (j & 1)); };
+        f32x16 s = zero16();
+        bf16x8 vop[kStream ? kRing : 2 * ND];
+        if constexpr (kStream) {
+          // d = 256 (one wave per SIMD, the whole register file): operands stream through a
+          // ring of kRing registers, read kAhead products ahead, so that the Q operands keep
+          // their VGPRs.
+          bf16x8 kop[kRing];
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
+          for (int i = 0; i < kAhead; ++i) kop[i] = lds_read_b128(kp + 16 * i);
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) vop[dt][c2] = lds_read_b128(vp + 32 * dt * VSTR + 16 * c2);
+          for (int cc = 0; cc < NC; ++cc) {
+            if (cc + kAhead < NC) kop[(cc + kAhead) % kRing] = lds_read_b128(kp + 16 * (cc + kAhead));
+            s = mfma32(kop[cc % kRing], qop[cc], s);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+          for (int i = 0; i < kAhead; ++i) vop[i] = vread(i);
+        } else {
+          bf16x8 kop[NC];
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) kop[cc] = lds_read_b128(kp + 16 * cc);
+          // Raised wave priority over each MFMA run: the other wave on the SIMD gets the
+          // softmax VALU slots while this one keeps the matrix core fed.
+          __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) s = mfma32(kop[cc], qop[cc], s);
+          __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+          for (int j = 0; j < 2 * ND; ++j) vop[j] = vread(j);
+        }
 
         // Online softmax.  In a piece that crosses the mask band (or the end of the
         // sequence) the masked scores are first replaced by -inf under a wave-uniform branch;
@@ -374,10 +395,16 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
 
         // O^T += V^T P^T.
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (kStream) {
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt) {
+          for (int j = 0; j < 2 * ND; ++j) {
+            if (j + kAhead < 2 * ND) vop[(j + kAhead) % kRing] = vread(j + kAhead);
+            acc[j >> 1] = mfma32(vop[j % kRing], pp[j & 1], acc[j >> 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) acc[dt] = mfma32(vop[dt][c2], pp[c2], acc[dt]);
+          for (int j = 0; j < 2 * ND; ++j) acc[j >> 1] = mfma32(vop[j], pp[j & 1], acc[j >> 1]);
         }
         __builtin_amdgcn_s_setprio(0);
       }
