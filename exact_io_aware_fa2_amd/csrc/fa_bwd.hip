@@ -143,6 +143,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int NC = D / 16;    // k-steps of S and dP over the head dim
   constexpr int NDH = DH / 32;  // owned 32-wide head-dim tiles of dK^T / dV^T
   constexpr int BUFB = Cfg::BUF * 2 + 2 * BQ * 4;  // bytes per buffer
+  constexpr int kRing = 4, kAh = 3;  // operand rings (see the step loop)
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int num_kb = (Nmax + BKN - 1) / BKN;
@@ -285,12 +286,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int mt = 0; mt < MT; ++mt) {
         const bf16_t* qa = sQ + (32 * mt + l32) * STR + 8 * hh;
         const bf16_t* oa = sO + (32 * mt + l32) * STR + 8 * hh;
-        bf16x8 qa_op[NC], oa_op[NC];
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          qa_op[cc] = lds_read_b128(qa + 16 * cc);
-          oa_op[cc] = lds_read_b128(oa + 16 * cc);
-        }
         s[mt] = zero16();
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {  // dP - D straight out of the products
@@ -298,10 +293,26 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) dp[mt][4 * g4 + e] = nd4[e];
         }
+        // The Q / dO operands stream through rings of kRing registers read kAh k-steps
+        // ahead (a scheduling barrier per k-step keeps the reads from being hoisted or sunk):
+        // with K and V resident the register file has no room for all of them at once, and
+        // reads placed right before their products leave the LDS latency exposed with one
+        // wave per SIMD.
+        bf16x8 qa_op[kRing], oa_op[kRing];
+#pragma unroll
+        for (int i = 0; i < kAh; ++i) {
+          qa_op[i] = lds_read_b128(qa + 16 * i);
+          oa_op[i] = lds_read_b128(oa + 16 * i);
+        }
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) {
-          s[mt] = mfma32(qa_op[cc], kop[cc], s[mt]);
-          dp[mt] = mfma32(oa_op[cc], vop[cc], dp[mt]);
+          if (cc + kAh < NC) {
+            qa_op[(cc + kAh) % kRing] = lds_read_b128(qa + 16 * (cc + kAh));
+            oa_op[(cc + kAh) % kRing] = lds_read_b128(oa + 16 * (cc + kAh));
+          }
+          s[mt] = mfma32(qa_op[cc % kRing], kop[cc], s[mt]);
+          dp[mt] = mfma32(oa_op[cc % kRing], vop[cc], dp[mt]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // P = exp2(S c + bias - LSE log2 e), masked entries 0 (selects under a wave-uniform
@@ -362,21 +373,27 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the owned head-dim slice (A operands from
       // the transposed tiles: the 8 rows of a k-step are contiguous).
+      // Product j = (head-dim tile j / (2 MT), k-step j % (2 MT)); operands through rings.
+      constexpr int NJ = NDH * 2 * MT;
+      auto aread = [&](const bf16_t* base, int j) {
+        return lds_read_b128(base + (32 * (j / (2 * MT)) + l32) * TSTR + 8 * hh + 16 * (j % (2 * MT)));
+      };
+      bf16x8 ao[kRing], aq[kRing];
 #pragma unroll
-      for (int dt = 0; dt < NDH; ++dt) {
-        const bf16_t* oa = sOT + (32 * dt + l32) * TSTR + 8 * hh;
-        const bf16_t* qa = sQT + (32 * dt + l32) * TSTR + 8 * hh;
-        bf16x8 ao[2 * MT], aq[2 * MT];
+      for (int i = 0; i < kAh; ++i) {
+        ao[i] = aread(sOT, i);
+        aq[i] = aread(sQT, i);
+      }
 #pragma unroll
-        for (int kstep = 0; kstep < 2 * MT; ++kstep) {
-          ao[kstep] = lds_read_b128(oa + 16 * kstep);
-          aq[kstep] = lds_read_b128(qa + 16 * kstep);
+      for (int j = 0; j < NJ; ++j) {
+        if (j + kAh < NJ) {
+          ao[(j + kAh) % kRing] = aread(sOT, j + kAh);
+          aq[(j + kAh) % kRing] = aread(sQT, j + kAh);
         }
-#pragma unroll
-        for (int kstep = 0; kstep < 2 * MT; ++kstep) {
-          dv[dt] = mfma32(ao[kstep], pP[kstep >> 1][kstep & 1], dv[dt]);
-          dk[dt] = mfma32(aq[kstep], pS[kstep >> 1][kstep & 1], dk[dt]);
-        }
+        const int dt = j / (2 * MT), kstep = j % (2 * MT);
+        dv[dt] = mfma32(ao[j % kRing], pP[kstep >> 1][kstep & 1], dv[dt]);
+        dk[dt] = mfma32(aq[j % kRing], pS[kstep >> 1][kstep & 1], dk[dt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (it + 1 < total_it) {
@@ -902,6 +919,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
         // (two named buffers, a scheduling barrier per step), as in the key-block kernel.
         // dP^T - D comes straight out of the products: the accumulator starts at -D.
         constexpr bool kAhead = D <= 128;
+        constexpr int kRing = 4, kAh = 3;  // d = 256 operand ring (see below)
         f32x16 s = zero16(), dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) dp[r] = ndval;
@@ -923,22 +941,37 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
           }
           __builtin_amdgcn_s_setprio(0);
         } else {
+          // d = 256: the K / V operands stream through rings of kRing registers, read kAh
+          // k-steps ahead, which leaves the Q and dO operands their VGPRs.
+          bf16x8 ok[kRing], ov[kRing];
+#pragma unroll
+          for (int i = 0; i < kAh; ++i) {
+            ok[i] = lds_read_b128(kp + 16 * i);
+            ov[i] = lds_read_b128(vp + 16 * i);
+          }
           __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int cc = 0; cc < NC; ++cc) {
-            s = mfma32(lds_read_b128(kp + 16 * cc), qop[cc], s);
-            dp = mfma32(lds_read_b128(vp + 16 * cc), oop[cc], dp);
+            if (cc + kAh < NC) {
+              ok[(cc + kAh) % kRing] = lds_read_b128(kp + 16 * (cc + kAh));
+              ov[(cc + kAh) % kRing] = lds_read_b128(vp + 16 * (cc + kAh));
+            }
+            s = mfma32(ok[cc % kRing], qop[cc], s);
+            dp = mfma32(ov[cc % kRing], oop[cc], dp);
+            __builtin_amdgcn_sched_barrier(0);
           }
           __builtin_amdgcn_s_setprio(0);
         }
         const bf16_t* tp = sKT + l32 * TSTR + 8 * hh + 32 * kt;
-        constexpr int NTA = kAhead ? ND : 1;
-        bf16x8 ta[NTA][2];
+        // K^T operand j = 2 dt + c2 (head-dim tile dt, key half c2)
+        auto tread = [&](int j) { return lds_read_b128(tp + 32 * (j >> 1) * TSTR + 16 * (j & 1)); };
+        bf16x8 ta[kAhead ? 2 * ND : kRing];
         if constexpr (kAhead) {
 #pragma unroll
-          for (int dt = 0; dt < ND; ++dt)
+          for (int j = 0; j < 2 * ND; ++j) ta[j] = tread(j);
+        } else {
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) ta[dt][c2] = lds_read_b128(tp + 32 * dt * TSTR + 16 * c2);
+          for (int i = 0; i < kAh; ++i) ta[i] = tread(i);
         }
         // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D); masked entries 0.
         float p[16];
@@ -973,15 +1006,17 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
         }
         // dQ^T += K^T dS^T
         __builtin_amdgcn_s_setprio(1);
+        if constexpr (kAhead) {
 #pragma unroll
-        for (int dt = 0; dt < ND; ++dt)
+          for (int j = 0; j < 2 * ND; ++j) acc[j >> 1] = mfma32(ta[j], pS[j & 1], acc[j >> 1]);
+        } else {
 #pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            if constexpr (kAhead)
-              acc[dt] = mfma32(ta[dt][c2], pS[c2], acc[dt]);
-            else
-              acc[dt] = mfma32(lds_read_b128(tp + 32 * dt * TSTR + 16 * c2), pS[c2], acc[dt]);
+          for (int j = 0; j < 2 * ND; ++j) {
+            if (j + kAh < 2 * ND) ta[(j + kAh) % kRing] = tread(j + kAh);
+            acc[j >> 1] = mfma32(ta[j % kRing], pS[j & 1], acc[j >> 1]);
+            __builtin_amdgcn_sched_barrier(0);
           }
+        }
         __builtin_amdgcn_s_setprio(0);
       }
     }
