@@ -98,6 +98,46 @@ def mfma_probe(fa, torch, dev, stream, blocks: int = 2048, iters: int = 20000, r
     return flop / (best * 1e-3) / 1e12
 
 
+ISSUE_PROBES = {  # kind: (name, params) of fa_issue_probe
+    0: ("fma_per_mfma", (0, 2, 4, 6, 8, 12)),
+    1: ("exp_per_mfma", (1, 2, 3, 4, 6, 8)),
+    2: ("chains", (1, 2, 4, 8)),
+    3: ("lds_operands_per_mfma", (0, 1, 2)),
+}
+
+
+def issue_probe(fa, torch, dev, stream, iters: int = 4000, reps: int = 3):
+    """Matrix-core throughput (fraction of the 2516.6 TFLOP/s peak, best of reps) with the
+    fa_issue_probe variants, one workgroup per CU at one and two waves per SIMD."""
+    blocks = 256
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    sh = stream.cuda_stream
+    res = {}
+    for kind, (name, params) in ISSUE_PROBES.items():
+        res[name] = {}
+        for wps in (1, 2):
+            row = {}
+            for param in params:
+                if fa.fa_issue_probe(out, kind, param, wps, blocks, 20, sh) != fa.FA_OK:
+                    raise RuntimeError(fa.fa_last_error())
+                best = None
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    if fa.fa_issue_probe(out, kind, param, wps, blocks, iters, sh) != fa.FA_OK:
+                        raise RuntimeError(fa.fa_last_error())
+                    e1.record(stream)
+                    e1.synchronize()
+                    ms = e0.elapsed_time(e1)
+                    best = ms if best is None else min(best, ms)
+                rounds = iters + (iters & 1) if kind == 3 else iters
+                products = 8 if kind == 2 else 4
+                flop = blocks * 4 * wps * rounds * products * 32768.0
+                row[str(param)] = round(flop / (best * 1e-3) / 1e12 / 2516.6, 4)
+            res[name][f"waves_per_simd_{wps}"] = row
+    return res
+
+
 def atomic_dq_count(w, bkn: int = 256, bq: int = 32) -> int:
     """float32 atomic adds an atomic accumulation of dQ would issue for a fixed-length
     workload: every key block of `bkn` keys adds, for each 32-row step it visits (the same
@@ -344,6 +384,8 @@ def run_decode(args, w):
                      "traffic": _traffic("decode_kernel", w.name, "fa_decode.hip"),
                      "algorithmic_bytes": nb, "avg_launch_ms": km},
     }
+    if args.probe_issue:
+        out["issue_probe_frac_of_peak"] = issue_probe(fa, torch, dev, stream)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -369,6 +411,9 @@ def main() -> int:
     ap.add_argument("--probe-atomic-dq", action="store_true",
                     help="also time float32 atomics in the pattern of an atomic dQ and price "
                          "that alternative to the separate dQ pass at this workload")
+    ap.add_argument("--probe-issue", action="store_true",
+                    help="also run the fa_issue_probe table: matrix-core throughput next to "
+                         "FMAs, exp2, LDS operand reads, and over dependent chains")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -577,6 +622,8 @@ def main() -> int:
             "note": "time of the atomic adds alone, at the probe's rate; an atomic dQ would "
                     "also add the dQ products and a transpose of dS to the key-block kernel, "
                     "and a zeroing and a conversion pass of the float32 accumulator"}
+    if args.probe_issue:
+        out["issue_probe_frac_of_peak"] = issue_probe(fa, torch, dev, stream)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

@@ -331,6 +331,29 @@ fa_status fa_atomic_probe(float* acc, int row_blocks, int stride, int blocks, in
                                                              iters, (hipStream_t)stream));
 }
 
+// The (kind, param) pairs fa_issue_probe has kernels for.
+static bool issue_probe_supported(int kind, int param) {
+  switch (kind) {
+    case 0: return param == 0 || param == 2 || param == 4 || param == 6 || param == 8 || param == 12;
+    case 1: return param == 1 || param == 2 || param == 3 || param == 4 || param == 6 || param == 8;
+    case 2: return param == 1 || param == 2 || param == 4 || param == 8;
+    case 3: return param == 0 || param == 1 || param == 2;
+    default: return false;
+  }
+}
+
+fa_status fa_issue_probe(float* out, int kind, int param, int waves_per_simd, int blocks,
+                         int iters, void* stream) {
+  if (!out) return fail(FA_ERR_INVALID_ARG, "fa_issue_probe: null pointer");
+  if (!issue_probe_supported(kind, param))
+    return fail(FA_ERR_UNSUPPORTED, "fa_issue_probe: unsupported (kind, param)");
+  if ((waves_per_simd != 1 && waves_per_simd != 2) || blocks <= 0 || iters <= 0)
+    return fail(FA_ERR_INVALID_ARG,
+                "fa_issue_probe: waves_per_simd must be 1 or 2, blocks and iters positive");
+  return launched("fa_issue_probe", fa::launch_issue_probe(out, kind, param, waves_per_simd,
+                                                           blocks, iters, (hipStream_t)stream));
+}
+
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
                         int Hkv, int d, int causal, int window, float scale, void* stream) {

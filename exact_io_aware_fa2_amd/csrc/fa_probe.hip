@@ -4,7 +4,10 @@
 //     published peak;
 //   * a kernel that only issues float32 atomic adds in the pattern an atomic accumulation
 //     of dQ would have (the alternative to the separate dQ pass of the backward), so the
-//     choice between the two can be priced with a measured atomic rate.
+//     choice between the two can be priced with a measured atomic rate;
+//   * issue probes: matrix products next to the other work the attention kernels put
+//     beside them (FMAs, exp2, LDS operand reads) and dependent product chains, to measure
+//     how much of that work the matrix core's issue pattern leaves room for.
 #include <hip/hip_runtime.h>
 
 #include "fa_common.hpp"
@@ -72,6 +75,178 @@ hipError_t launch_atomic_probe(float* acc, int row_blocks, int stride, int block
   hipLaunchKernelGGL(atomic_probe_kernel, dim3(blocks), dim3(256), 0, st, acc, row_blocks,
                      stride, iters);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------
+// Issue probes.  Every wave runs `iters` rounds of four v_mfma_f32_32x32x16_bf16 products
+// (kChains accumulation chains unless stated) and writes one float per lane so that no work
+// is optimised away.  The caller sizes the grid (one workgroup of 64 * waves-per-SIMD * 4
+// threads per CU for the published figures) and times the launch.
+
+// kind 0 / 1: each product is followed by NV independent FMAs (EXP = false) or v_exp_f32
+// (EXP = true) on eight rotating registers; scheduling-group barriers keep the
+// interleave (one product, then its NV VALU instructions).
+template <int NV, bool EXP>
+__global__ __launch_bounds__(512) void issue_valu_kernel(float* __restrict__ out, int iters) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (int)(threadIdx.x + i));
+    b[i] = (__bf16)(0.002f * i);
+  }
+  f32x16 acc[kProbeChains];
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j) acc[j] = zero16();
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 0.5f + 0.01f * (float)((threadIdx.x + i) & 31);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < kProbeChains; ++j) {
+      acc[j] = mfma32(a, b, acc[j]);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int i = (j * NV + v) & 7;
+        // exp2 of a value in (0, 1] stays in [0.5, 1]: bounded, never denormal
+        x[i] = EXP ? __builtin_amdgcn_exp2f(-x[i]) : __builtin_fmaf(x[i], 0.999f, 0.001f);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);  // then NV VALU
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += x[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// kind 2: eight products per round spread over NCH accumulation chains (NCH = 1: each
+// product depends on the one before it).
+template <int NCH>
+__global__ __launch_bounds__(512) void issue_chain_kernel(float* __restrict__ out, int iters) {
+  bf16x8 a[8], b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    b[i] = (__bf16)(0.002f * i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j][i] = (__bf16)(0.001f * (int)(threadIdx.x + i + j));
+  }
+  f32x16 acc[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) acc[c] = zero16();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k % NCH] = mfma32(a[k], b, acc[k % NCH]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// kind 3: NR of each product's operands (A, then B) come from LDS as 16-byte reads
+// (consecutive lanes, consecutive 16-byte chunks of a 1 KiB run per wave), issued one
+// round ahead into a second register set, as the attention kernels stage their operands.
+// The workgroup uses 64 KiB of LDS; every address stays inside it.
+constexpr int kIssueLdsBytes = 65536;
+
+template <int NR>
+__global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out, int iters) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int i = t; i < kIssueLdsBytes / 4; i += blockDim.x)
+    reinterpret_cast<float*>(smem)[i] = 0.001f * (float)(i & 255);
+  __syncthreads();
+  // byte offset of operand r of chain c in round it: a 1 KiB-aligned run per wave
+  auto off = [&](int it, int c, int r) {
+    return ((w * 1024 + c * 8192 + r * 4096 + (it & 3) * 2048) & (kIssueLdsBytes - 1024)) +
+           lane * 16;
+  };
+  auto rd = [&](int it, int c, int r) { return lds_read_b128(smem + off(it, c, r)); };
+  bf16x8 k0, k1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    k0[i] = (__bf16)(0.001f * (int)(t + i));
+    k1[i] = (__bf16)(0.002f * i);
+  }
+  f32x16 acc[kProbeChains];
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j) acc[j] = zero16();
+  bf16x8 sa[2][kProbeChains], sb[2][kProbeChains];
+  auto load = [&](int set, int it) {
+#pragma unroll
+    for (int j = 0; j < kProbeChains; ++j) {
+      if (NR >= 1) sa[set][j] = rd(it, j, 0);
+      if (NR >= 2) sb[set][j] = rd(it, j, 1);
+    }
+  };
+  auto products = [&](int set) {
+#pragma unroll
+    for (int j = 0; j < kProbeChains; ++j)
+      acc[j] = mfma32(NR >= 1 ? sa[set][j] : k0, NR >= 2 ? sb[set][j] : k1, acc[j]);
+  };
+  load(0, 0);
+  for (int it = 0; it < iters; it += 2) {
+    load(1, it + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    products(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, it + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    products(1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  out[blockIdx.x * blockDim.x + t] = s;
+}
+
+template <typename Kernel>
+static hipError_t launch_issue(Kernel k, int blocks, int threads, size_t lds, float* out,
+                               int iters, hipStream_t st) {
+  if (lds > 0) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k, dim3(blocks), dim3(threads), lds, st, out, iters);
+  return hipGetLastError();
+}
+
+hipError_t launch_issue_probe(float* out, int kind, int param, int waves_per_simd, int blocks,
+                              int iters, hipStream_t st) {
+  const int threads = 256 * waves_per_simd;
+  switch (kind * 100 + param) {
+    case 0: return launch_issue(issue_valu_kernel<0, false>, blocks, threads, 0, out, iters, st);
+    case 2: return launch_issue(issue_valu_kernel<2, false>, blocks, threads, 0, out, iters, st);
+    case 4: return launch_issue(issue_valu_kernel<4, false>, blocks, threads, 0, out, iters, st);
+    case 6: return launch_issue(issue_valu_kernel<6, false>, blocks, threads, 0, out, iters, st);
+    case 8: return launch_issue(issue_valu_kernel<8, false>, blocks, threads, 0, out, iters, st);
+    case 12: return launch_issue(issue_valu_kernel<12, false>, blocks, threads, 0, out, iters, st);
+    case 101: return launch_issue(issue_valu_kernel<1, true>, blocks, threads, 0, out, iters, st);
+    case 102: return launch_issue(issue_valu_kernel<2, true>, blocks, threads, 0, out, iters, st);
+    case 103: return launch_issue(issue_valu_kernel<3, true>, blocks, threads, 0, out, iters, st);
+    case 104: return launch_issue(issue_valu_kernel<4, true>, blocks, threads, 0, out, iters, st);
+    case 106: return launch_issue(issue_valu_kernel<6, true>, blocks, threads, 0, out, iters, st);
+    case 108: return launch_issue(issue_valu_kernel<8, true>, blocks, threads, 0, out, iters, st);
+    case 201: return launch_issue(issue_chain_kernel<1>, blocks, threads, 0, out, iters, st);
+    case 202: return launch_issue(issue_chain_kernel<2>, blocks, threads, 0, out, iters, st);
+    case 204: return launch_issue(issue_chain_kernel<4>, blocks, threads, 0, out, iters, st);
+    case 208: return launch_issue(issue_chain_kernel<8>, blocks, threads, 0, out, iters, st);
+    case 300: return launch_issue(issue_lds_kernel<0>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    case 301: return launch_issue(issue_lds_kernel<1>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    case 302: return launch_issue(issue_lds_kernel<2>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fa

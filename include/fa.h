@@ -64,7 +64,7 @@ typedef enum {
   FA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, non-positive size, Hq % Hkv != 0,
                              window < 0, non-finite scale, size product overflowing 2^31
                              elements                                                   */
-  FA_ERR_UNSUPPORTED = 2, /* head dim outside {64, 128, 256}                             */
+  FA_ERR_UNSUPPORTED = 2, /* head dim outside {64, 128, 256}; a probe variant not built   */
   FA_ERR_WORKSPACE = 3,   /* workspace missing, too small or not 256-byte aligned        */
   FA_ERR_HIP = 4          /* the HIP runtime reported an error at launch                  */
 } fa_status;
@@ -290,6 +290,26 @@ fa_status fa_mfma_probe(float* out, int blocks, int iters, void* stream);
  */
 fa_status fa_atomic_probe(float* acc, int row_blocks, int stride, int blocks, int iters,
                           void* stream);
+
+/*
+ * Measurement aid (no counterpart on the pages): how much other work the matrix core's
+ * issue pattern leaves room for.  Enqueues `blocks` workgroups of 256 * waves_per_simd
+ * threads (waves_per_simd 1 or 2; with `blocks` = 256 that is one workgroup per CU); every
+ * wave runs `iters` rounds of four v_mfma_f32_32x32x16_bf16 products (4 * 32768 flop per
+ * wave and round) and writes one float per lane to `out`, which must hold
+ * blocks * 256 * waves_per_simd floats.  `kind` selects what sits beside the products:
+ *   0  param in {0,2,4,6,8,12}: param independent float32 FMAs after each product;
+ *   1  param in {1,2,3,4,6,8}:  param independent v_exp_f32 after each product;
+ *   2  param in {1,2,4,8}:      the round's products spread over param accumulation
+ *                               chains (eight products per round for this kind);
+ *   3  param in {0,1,2}:        param operands of each product read from LDS (16 bytes per
+ *                               lane, one round ahead; 64 KiB of LDS per workgroup; iters
+ *                               is rounded up to an even count).
+ * The caller times the launch.  FA_ERR_UNSUPPORTED for another (kind, param),
+ * FA_ERR_INVALID_ARG for a null pointer, waves_per_simd not 1 or 2, or non-positive counts.
+ */
+fa_status fa_issue_probe(float* out, int kind, int param, int waves_per_simd, int blocks,
+                         int iters, void* stream);
 
 /* Message for the last non-FA_OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);

@@ -122,6 +122,18 @@ def test_atomic_probe_validation():
     assert "2^31" in fa.fa_last_error()
 
 
+def test_issue_probe_validation():
+    # every rejection happens before a launch (no GPU here)
+    assert fa.fa_issue_probe(None, 0, 4, 2, 4, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    for kind, param in ((0, 3), (1, 0), (2, 3), (3, 3), (4, 0), (-1, 0)):
+        assert fa.fa_issue_probe(1 << 20, kind, param, 2, 4, 4, stream=0) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_issue_probe(1 << 20, 0, 4, 3, 4, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_issue_probe(1 << 20, 0, 4, 0, 4, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_issue_probe(1 << 20, 0, 4, 2, 0, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_issue_probe(1 << 20, 0, 4, 2, 4, 0, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_last_error().startswith("fa_issue_probe")
+
+
 BAD_VARLEN = [
     (dict(cu=None), fa.FA_ERR_INVALID_ARG),
     (dict(num_seqs=0), fa.FA_ERR_INVALID_ARG),
