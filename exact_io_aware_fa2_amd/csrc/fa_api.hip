@@ -354,6 +354,20 @@ fa_status fa_issue_probe(float* out, int kind, int param, int waves_per_simd, in
                                                            blocks, iters, (hipStream_t)stream));
 }
 
+fa_status fa_fp8_product_probe(const void* a, const void* bt, float* c, int sets,
+                               void* stream) {
+  if (!a || !bt || !c) return fail(FA_ERR_INVALID_ARG, "fa_fp8_product_probe: null pointer");
+  if (sets <= 0) return fail(FA_ERR_INVALID_ARG, "fa_fp8_product_probe: sets must be positive");
+  if (sat_mul({sets, 2048}) >= kMaxElems)
+    return fail(FA_ERR_INVALID_ARG, "fa_fp8_product_probe: sets * 2048 reaches 2^31");
+  if (misaligned({a, bt}, 16) || misaligned({c}, 4))
+    return fail(FA_ERR_INVALID_ARG, "fa_fp8_product_probe: misaligned pointer");
+  return launched("fa_fp8_product_probe",
+                  fa::launch_fp8_product_probe(static_cast<const uint8_t*>(a),
+                                               static_cast<const uint8_t*>(bt), c, sets,
+                                               (hipStream_t)stream));
+}
+
 fa_status fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                         const int* cu_seqlens, int num_seqs, int total, int max_seqlen, int Hq,
                         int Hkv, int d, int causal, int window, float scale, void* stream) {

@@ -76,6 +76,8 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t st);
 hipError_t launch_mfma_probe(float* out, int blocks, int iters, hipStream_t st);
 hipError_t launch_issue_probe(float* out, int kind, int param, int waves_per_simd, int blocks,
                               int iters, hipStream_t st);
+hipError_t launch_fp8_product_probe(const uint8_t* a, const uint8_t* bt, float* c, int sets,
+                                    hipStream_t st);
 hipError_t launch_atomic_probe(float* acc, int row_blocks, int stride, int blocks, int iters,
                                hipStream_t st);
 

@@ -8,6 +8,9 @@
 //   * issue probes: matrix products next to the other work the attention kernels put
 //     beside them (FMAs, exp2, LDS operand reads) and dependent product chains, to measure
 //     how much of that work the matrix core's issue pattern leaves room for.
+//   * a kernel that runs single 32 x 32 x 64 products of 8-bit E4M3 operands given by the
+//     caller, so the accuracy of the 8-bit matrix core's 64-term sums can be checked
+//     against exact sums (the error bound the 8-bit forward's tolerances rest on).
 #include <hip/hip_runtime.h>
 
 #include "fa_common.hpp"
@@ -247,6 +250,48 @@ hipError_t launch_issue_probe(float* out, int kind, int param, int waves_per_sim
     case 302: return launch_issue(issue_lds_kernel<2>, blocks, threads, kIssueLdsBytes, out, iters, st);
     default: return hipErrorInvalidValue;
   }
+}
+
+// ---------------------------------------------------------------------------------
+// 8-bit product probe: wave w of workgroup g computes set 4 g + w, C = A B with
+// A[m][k] = a[set][m][k] and B[k][n] = bt[set][n][k] (32 x 64 codes each, row-major per set),
+// as one v_mfma_f32_32x32x64_f8f6f4 from a zero accumulator, and writes C[m][n] as float32
+// to c[set][m][n].  Lane l holds row / column l % 32 of each operand and its 32 bytes
+// k = 32 (l / 32) + byte; the result is in the accumulator layout of the bf16 product.
+typedef int i32x8p __attribute__((ext_vector_type(8)));
+typedef float f32v16p __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(256) void fp8_product_kernel(const uint8_t* __restrict__ a,
+                                                          const uint8_t* __restrict__ bt,
+                                                          float* __restrict__ c, int sets) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int set = blockIdx.x * 4 + w;
+  if (set >= sets) return;  // whole wave
+  const size_t base = (size_t)set * 2048 + (size_t)(l & 31) * 64 + 32 * (l >> 5);
+  const uint4 a0 = *reinterpret_cast<const uint4*>(a + base);
+  const uint4 a1 = *reinterpret_cast<const uint4*>(a + base + 16);
+  const uint4 b0 = *reinterpret_cast<const uint4*>(bt + base);
+  const uint4 b1 = *reinterpret_cast<const uint4*>(bt + base + 16);
+  const i32x8p ao = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w,
+                     (int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+  const i32x8p bo = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                     (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+  f32v16p z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  const f32v16p r = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ao, bo, z, 0, 0, 0, 0, 0, 0);
+  float* cs = c + (size_t)set * 1024;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int m = 8 * (i >> 2) + 4 * (l >> 5) + (i & 3), n = l & 31;
+    cs[m * 32 + n] = r[i];
+  }
+}
+
+hipError_t launch_fp8_product_probe(const uint8_t* a, const uint8_t* bt, float* c, int sets,
+                                    hipStream_t st) {
+  hipLaunchKernelGGL(fp8_product_kernel, dim3((sets + 3) / 4), dim3(256), 0, st, a, bt, c, sets);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -27,7 +27,8 @@ EXPORTED = ("fa_fwd", "fa_fwd_alibi", "fa_fwd_fp32", "fa_fwd_fp8", "fa_decode",
             "fa_bwd_noalloc", "fa_bwd_workspace_size", "fa_fwd_varlen", "fa_fwd_varlen_alibi",
             "fa_bwd_varlen",
             "fa_bwd_varlen_alibi", "fa_bwd_varlen_workspace_size", "fa_bwd_time_main_kernel",
-            "fa_mfma_probe", "fa_atomic_probe", "fa_issue_probe", "fa_last_error", "fa_version")
+            "fa_mfma_probe", "fa_atomic_probe", "fa_issue_probe", "fa_fp8_product_probe", "fa_last_error",
+            "fa_version")
 
 
 class FaError(RuntimeError):
@@ -93,6 +94,8 @@ def load() -> ctypes.CDLL:
     lib.fa_atomic_probe.restype = i
     lib.fa_issue_probe.argtypes = [vp, i, i, i, i, i, vp]
     lib.fa_issue_probe.restype = i
+    lib.fa_fp8_product_probe.argtypes = [vp, vp, vp, i, vp]
+    lib.fa_fp8_product_probe.restype = i
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -243,6 +246,10 @@ def fa_mfma_probe(out, blocks, iters, stream=None) -> int:
 def fa_atomic_probe(acc, row_blocks, stride, blocks, iters, stream=None) -> int:
     return load().fa_atomic_probe(_ptr(acc), int(row_blocks), int(stride), int(blocks),
                                   int(iters), _stream(stream))
+
+
+def fa_fp8_product_probe(a, bt, c, sets, stream=None) -> int:
+    return load().fa_fp8_product_probe(_ptr(a), _ptr(bt), _ptr(c), int(sets), _stream(stream))
 
 
 def fa_issue_probe(out, kind, param, waves_per_simd, blocks, iters, stream=None) -> int:

@@ -311,6 +311,18 @@ fa_status fa_atomic_probe(float* acc, int row_blocks, int stride, int blocks, in
 fa_status fa_issue_probe(float* out, int kind, int param, int waves_per_simd, int blocks,
                          int iters, void* stream);
 
+/*
+ * Measurement aid for the 8-bit forward's error bound (no counterpart on the pages): one
+ * v_mfma_f32_32x32x64_f8f6f4 per operand set from a zero accumulator, C = A B with
+ * A[m][k] = a[s][m][k] and B[k][n] = bt[s][n][k] for s < sets (E4M3 codes, 32 x 64 bytes per
+ * set and operand, row-major), written as float32 to c[s][m][n] (32 x 32 per set).  The
+ * caller owns the device buffers: a and bt hold sets * 2048 bytes and are 16-byte aligned, c
+ * holds sets * 1024 floats.  FA_ERR_INVALID_ARG for a null or misaligned pointer,
+ * sets <= 0 or sets * 2048 >= 2^31.
+ */
+fa_status fa_fp8_product_probe(const void* a, const void* bt, float* c, int sets,
+                               void* stream);
+
 /* Message for the last non-FA_OK status returned on this thread ("" if none). */
 const char* fa_last_error(void);
 

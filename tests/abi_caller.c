@@ -53,6 +53,13 @@ typedef fa_status (*fwd_fp8_fn)(const void*, const void*, const void*, void*, fl
 typedef fa_status (*decode_fn)(const void*, const void*, const void*, const int*, void*, float*,
                                int, int, int, int, int, int, int, int, float, int, void*,
                                size_t, void*);
+typedef fa_status (*bwd_noalloc_fn)(const void*, const void*, const void*, const void*,
+                                    const void*, const float*, void*, void*, void*, int, int,
+                                    int, int, int, int, int, float, void*);
+typedef fa_status (*mfma_probe_fn)(float*, int, int, void*);
+typedef fa_status (*atomic_probe_fn)(float*, int, int, int, int, void*);
+typedef fa_status (*issue_probe_fn)(float*, int, int, int, int, int, void*);
+typedef fa_status (*fp8_product_probe_fn)(const void*, const void*, float*, int, void*);
 typedef const char* (*str_fn)(void);
 
 static const fwd_fn p_fwd = fa_fwd;
@@ -67,6 +74,11 @@ static const fwd_varlen_alibi_fn p_fwd_varlen_alibi = fa_fwd_varlen_alibi;
 static const bwd_varlen_alibi_fn p_bwd_varlen_alibi = fa_bwd_varlen_alibi;
 static const fwd_fp8_fn p_fwd_fp8 = fa_fwd_fp8;
 static const decode_fn p_decode = fa_decode;
+static const bwd_noalloc_fn p_bwd_noalloc = fa_bwd_noalloc;
+static const mfma_probe_fn p_mfma_probe = fa_mfma_probe;
+static const atomic_probe_fn p_atomic_probe = fa_atomic_probe;
+static const issue_probe_fn p_issue_probe = fa_issue_probe;
+static const fp8_product_probe_fn p_fp8_probe = fa_fp8_product_probe;
 static const str_fn p_err = fa_last_error;
 static const str_fn p_ver = fa_version;
 
@@ -167,6 +179,20 @@ int main(void) {
          p_bwd_varlen_alibi(A, A, A, A, A, F, A, A, A, I, 3, 64, 40, 4, 2, 128, 1, 0, 0.1f, A,
                             1 << 20, NULL, S),
          FA_ERR_INVALID_ARG, "alibi_slopes");
+
+  expect("bwd_noalloc too many rows",
+         p_bwd_noalloc(A, A, A, A, A, F, A, A, A, 64, 64, 64, 2048, 128, 1, 0, 0.1f, S),
+         FA_ERR_WORKSPACE, "fa_bwd_noalloc");
+  expect("bwd_noalloc null pointer",
+         p_bwd_noalloc(NULL, A, A, A, A, F, A, A, A, 1, 4, 2, 128, 128, 1, 0, 0.1f, S),
+         FA_ERR_INVALID_ARG, "fa_bwd_noalloc");
+  expect("mfma_probe null", p_mfma_probe(NULL, 4, 4, S), FA_ERR_INVALID_ARG, "fa_mfma_probe");
+  expect("atomic_probe narrow stride", p_atomic_probe(F, 8, 64, 4, 4, S), FA_ERR_INVALID_ARG,
+         "fa_atomic_probe");
+  expect("issue_probe unknown kind", p_issue_probe(F, 9, 0, 2, 4, 4, S), FA_ERR_UNSUPPORTED,
+         "fa_issue_probe");
+  expect("fp8_product_probe no sets", p_fp8_probe(A, A, F, 0, S), FA_ERR_INVALID_ARG,
+         "fa_fp8_product_probe");
 
   expect("decode Nq=0",
          p_decode(A, A, A, NULL, A, F, 2, 8, 2, 0, 4096, 128, 1, 0, 0.1f, 4, A, 1 << 20, S),

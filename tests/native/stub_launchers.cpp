@@ -42,6 +42,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t) {
 hipError_t launch_mfma_probe(float*, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_atomic_probe(float*, int, int, int, int, hipStream_t) { return hipSuccess; }
 hipError_t launch_issue_probe(float*, int, int, int, int, int, hipStream_t) { return hipSuccess; }
+hipError_t launch_fp8_product_probe(const uint8_t*, const uint8_t*, float*, int, hipStream_t) {
+  return hipSuccess;
+}
 // The static workspace of the no-allocation backward: a host address that only flows into the
 // recorded arguments.
 hipError_t noalloc_scratch(float** ptr) {

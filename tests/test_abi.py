@@ -134,6 +134,18 @@ def test_issue_probe_validation():
     assert fa.fa_last_error().startswith("fa_issue_probe")
 
 
+def test_fp8_product_probe_validation():
+    good = 1 << 20
+    assert fa.fa_fp8_product_probe(None, good, good, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fp8_product_probe(good, None, good, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fp8_product_probe(good, good, None, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fp8_product_probe(good, good, good, 0, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fp8_product_probe(good, good, good, 1 << 20, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fp8_product_probe(good + 8, good, good, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_fp8_product_probe(good, good, good + 2, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_last_error().startswith("fa_fp8_product_probe")
+
+
 BAD_VARLEN = [
     (dict(cu=None), fa.FA_ERR_INVALID_ARG),
     (dict(num_seqs=0), fa.FA_ERR_INVALID_ARG),

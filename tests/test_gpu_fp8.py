@@ -71,7 +71,8 @@ def _check_random(shape, codes, factors, scale):
     worst = 0.0
     for b in range(B):
         for h in range(Hq):
-            delta = fp8_score_error(qd[b, :, h], kd[b, :, h // g], scale)
+            delta = fp8_score_error(qd[b, :, h], kd[b, :, h // g], scale, float(factors[0]),
+                                   float(factors[1]))
             check_fp8_lse(lse64[b, h], lse_ref[b, h], delta)
             p = oracle.attention_probs(qd[b, :, h], kd[b, :, h // g], causal, window, scale)
             bound = fp8_o_bound(p, vd[b, :, h // g], o_ref[b, :, h], delta)
@@ -155,7 +156,8 @@ def test_fp8_bench_workload_sampled():
         vd = oracle.dequantize(_codes(v8[b, :, h // g]), factors[2])
         o_ref, lse_ref = oracle.attn_fwd_rows(qd, kd, vd, rows, w.causal, w.window, w.scale)
         p = oracle.attention_probs_rows(qd, kd, rows, w.causal, w.window, w.scale)
-        delta = fp8_score_error(qd[rows], kd, w.scale)
+        delta = fp8_score_error(qd[rows], kd, w.scale, float(factors[0]),
+                                   float(factors[1]))
         check_fp8_o(o_c[b, rows, h].double().numpy(), o_ref, fp8_o_bound(p, vd, o_ref, delta),
                     f"O[b{b},h{h}]")
         check_fp8_lse(lse_c[b, h, rows].double().numpy(), lse_ref, delta)

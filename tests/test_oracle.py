@@ -620,13 +620,26 @@ def test_quantize_e4m3_roundtrip():
 
 
 def test_fp8_score_error_dominates_brute_force_terms():
+    # Delta_i >= (d/64) 2 * 2^-9 |scale| max_j max_c 2^(e(q_ic) + e(k_jc)) fq fk + 2^-22 max_j
+    # |s_ij|, with the exponents taken from the codes themselves (subnormal codes at -6)
     from tests._parity import fp8_score_error
-    rng = np.random.default_rng(43)
-    q, k = rng.standard_normal((50, 128)) * 3, rng.standard_normal((70, 128))
-    got = fp8_score_error(q, k, -0.2)
-    prod = np.abs(q[:, None, :] * k[None, :, :]).max(axis=2).max(axis=1)
+    torch = pytest.importorskip("torch")
+    from exact_io_aware_fa2_amd.workloads import quantize_e4m3
+    g = torch.Generator().manual_seed(43)
+    xq = torch.randn(50, 128, generator=g) * 3
+    xk = torch.randn(70, 128, generator=g)
+    xq[:, :5] *= 1e-4  # subnormal codes
+    (cq, fq), (ck, fk) = quantize_e4m3(xq), quantize_e4m3(xk)
+    cq, ck = cq.numpy(), ck.numpy()
+    q, k = e4m3_decode(cq) * fq, e4m3_decode(ck) * fk
+    assert ((cq & 0x78) == 0).any() and (q != 0).any()  # some subnormal codes present
+    got = fp8_score_error(q, k, -0.2, fq, fk)
+    eq = np.exp2(np.maximum((cq.astype(np.int64) >> 3) & 0xF, 1) - 7.0) * fq
+    ek = np.exp2(np.maximum((ck.astype(np.int64) >> 3) & 0xF, 1) - 7.0) * fk
+    align = (eq[:, None, :] * ek[None, :, :]).max(axis=2).max(axis=1)
     smax = np.abs(q @ k.T * 0.2).max(axis=1)
-    assert (got >= 2 * 2.0 ** -10 * 0.2 * prod + 2.0 ** -22 * smax - 1e-15).all()
+    need = (128 / 64) * 2 * 2.0 ** -9 * 0.2 * align + 2.0 ** -22 * smax
+    assert (got >= need * (1 - 1e-12)).all()
 
 
 # ------------------------------------------------------------------ ALiBi position bias
