@@ -17,10 +17,11 @@
 // accumulator, its atomics and its conversion pass, and keeps dQ deterministic.
 //
 // Key-block kernel: a workgroup = 8 waves = 256 keys of one (batch entry, KV head) for
-// d <= 128 (bwd_dkdv8_kernel), 4 waves = 128 keys and one half of the head dim of dK/dV for
-// d = 256 (bwd_dkdv_kernel); 32 keys per wave.  The wave's K rows are MFMA B operands in
-// VGPRs; dK^T and dV^T accumulate in registers across every query head of the GQA group
-// and every query block, and are written once.
+// d <= 128 (bwd_dkdv8_kernel), 4 waves = 128 keys for d = 256 (bwd_dkdv_kernel); 32 keys
+// per wave.  The wave's K rows are MFMA B operands in VGPRs; dK^T and dV^T accumulate in
+// registers across every query head of the GQA group and every query block, and are
+// written once.  At d = 256 those accumulators fill all 256 AGPRs of a wave (one wave per
+// SIMD), with K, V and the score work in the 256 VGPRs.
 //
 // Both grids follow work_item: each XCD owns a range of heads, heaviest blocks first.
 //
@@ -114,20 +115,47 @@ __device__ __forceinline__ int key_block(int rank, int num_kb, int nb, int causa
 
 // =====================================================================================
 // dK / dV
+
+// Matrix products whose accumulators live in AGPRs.  The compiler gives a kernel either
+// every product in the AGPR form or none, and the d = 256 key-block kernel needs its 256
+// dK/dV accumulator registers in AGPRs next to VGPR scores, so those products are inline
+// assembly.  The compiler does not see them as matrix instructions: the wait states the
+// hardware needs where vector instructions touch their registers are written out here.
+// acc += a b (v_mfma_f32_32x32x16_bf16 with an AGPR accumulator).
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// After vector writes of accumulators, before a product reads them.
+__device__ __forceinline__ void acc_written(f32x16 (&x)[8]) {
+  asm volatile("s_nop 4"
+               : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]),
+                 "+a"(x[6]), "+a"(x[7]));
+}
+// After the last product, before vector instructions read the accumulators (more wait
+// states than a 32x32x16 product's latency).
+__device__ __forceinline__ void acc_ready(f32x16 (&x)[8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]),
+                 "+a"(x[6]), "+a"(x[7]));
+}
+// After vector writes of product operands, before the products read them.
+__device__ __forceinline__ void operands_ready(bf16x8 (&p)[2], bf16x8 (&q)[2]) {
+  asm volatile("s_nop 1" : "+v"(p[0]), "+v"(p[1]), "+v"(q[0]), "+v"(q[1]));
+}
+
 template <int D>
 struct KVCfg {
   static constexpr int NT = 256;                 // 4 waves x 32 keys
   static constexpr int BKN = 128;                // keys per workgroup
-  static constexpr int DH = D <= 128 ? D : 128;  // head-dim slice of dK/dV per workgroup
-  static constexpr int NSPLIT = D / DH;
   static constexpr int BQ = D <= 128 ? 64 : 32;  // query rows per step
   static constexpr int MT = BQ / 32;             // 32-row MFMA tiles per step
   static constexpr int STR = D + 8;              // row-major Q / dO row stride (elements)
   static constexpr int TSTR = BQ + 8;            // transposed Q^T / dO^T row stride
   static constexpr int SQ = BQ * STR;
-  static constexpr int SQT = DH * TSTR;
+  static constexpr int SQT = D * TSTR;
   static constexpr int BUF = 2 * SQ + 2 * SQT;   // Q, dO, Q^T, dO^T (elements)
   static constexpr int LDS_BYTES = 2 * (BUF * 2 + 2 * BQ * 4);  // + LSE, D; double buffered
+  static_assert(LDS_BYTES <= 160 * 1024, "staging fits the CU's LDS");
 };
 
 template <int D, int AL>
@@ -138,25 +166,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     int causal, int window, float c, float scale, const int* __restrict__ cu, int ntot,
     const float* __restrict__ slopes) {
   using Cfg = KVCfg<D>;
-  constexpr int BKN = Cfg::BKN, BQ = Cfg::BQ, MT = Cfg::MT, DH = Cfg::DH;
-  constexpr int NSPLIT = Cfg::NSPLIT, STR = Cfg::STR, TSTR = Cfg::TSTR;
-  constexpr int NC = D / 16;    // k-steps of S and dP over the head dim
-  constexpr int NDH = DH / 32;  // owned 32-wide head-dim tiles of dK^T / dV^T
+  constexpr int BKN = Cfg::BKN, BQ = Cfg::BQ, MT = Cfg::MT;
+  constexpr int STR = Cfg::STR, TSTR = Cfg::TSTR;
+  constexpr int NC = D / 16;   // k-steps of S and dP over the head dim
+  constexpr int NDH = D / 32;  // 32-wide head-dim tiles of dK^T / dV^T
   constexpr int BUFB = Cfg::BUF * 2 + 2 * BQ * 4;  // bytes per buffer
   constexpr int kRing = 4, kAh = 3;  // operand rings (see the step loop)
+  // dK^T / dV^T in AGPRs through the assembly products (all 256 of them at d = 256)
+  constexpr bool kAcc = NDH == 8;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int num_kb = (Nmax + BKN - 1) / BKN;
-  // the head-dim splits of one key block are adjacent ranks of equal cost
-  int b, hkv, rs;
-  work_item(B, Hkv, num_kb * NSPLIT, b, hkv, rs);
-  const int split = rs % NSPLIT, rank = rs / NSPLIT;
+  int b, hkv, rank;
+  work_item(B, Hkv, num_kb, b, hkv, rank);
   int seq0, N;  // first row and length of this batch entry's sequence
   seq_span(cu, ntot, b, Nmax, seq0, N);
   const int kb = key_block(rank, num_kb, (N + BKN - 1) / BKN, causal, window);
   if (kb < 0 || kb * BKN >= N) return;  // no such block in a shorter packed sequence
   const int G = Hq / Hkv;
-  const int dh0 = split * DH;
 
   const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
   const int hh = lane >> 5, l32 = lane & 31;
@@ -196,9 +223,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     dk[i] = zero16();
     dv[i] = zero16();
   }
+  if constexpr (kAcc) {
+    acc_written(dk);
+    acc_written(dv);
+  }
 
-  // Staging: a task = 4 rows x 8 dims of Q and of dO, stored row-major and (for the owned
-  // head-dim slice) transposed.
+  // Staging: a task = 4 rows x 8 dims of Q and of dO, stored row-major and transposed.
   constexpr int CPR = D / 8;
   constexpr int TASKS = (BQ / 4) * CPR;
   static_assert(BQ % 16 == 0, "task_rc needs whole groups of 16 rows");
@@ -245,11 +275,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
         task_rc<CPR>(task, rg, dc);
         store_4x8_rows(sQ, STR, 4 * rg, 8 * dc, qr[p]);
         store_4x8_rows(sO, STR, 4 * rg, 8 * dc, orr[p]);
-        const int dl = 8 * dc - dh0;
-        if (NSPLIT == 1 || (dl >= 0 && dl < DH)) {
-          store_4x8_transposed(sQT, TSTR, 4 * rg, dl, qr[p]);
-          store_4x8_transposed(sOT, TSTR, 4 * rg, dl, orr[p]);
-        }
+        store_4x8_transposed(sQT, TSTR, 4 * rg, 8 * dc, qr[p]);
+        store_4x8_transposed(sOT, TSTR, 4 * rg, 8 * dc, orr[p]);
       }
     }
     if (tid < BQ) {
@@ -315,6 +342,16 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // A operands of the dV / dK products through rings: product j = (head-dim tile
+      // j / (2 MT), k-step j % (2 MT)).  The first slot is read here, so its latency hides
+      // behind the softmax (more slots this early spill at d = 256).
+      constexpr int NJ = NDH * 2 * MT;
+      auto aread = [&](const bf16_t* base, int j) {
+        return lds_read_b128(base + (32 * (j / (2 * MT)) + l32) * TSTR + 8 * hh + 16 * (j % (2 * MT)));
+      };
+      bf16x8 ao[kRing], aq[kRing];
+      ao[0] = aread(sOT, 0);
+      aq[0] = aread(sQT, 0);
       // P = exp2(S c + bias - LSE log2 e), masked entries 0 (selects under a wave-uniform
       // branch).  The position bias: see alibi_addend (here the lane is the key).
       const float sl2 = slope_of(it);
@@ -371,16 +408,11 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           pS[mt][c2][i0 + 3] = d23[1];
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the owned head-dim slice (A operands from
-      // the transposed tiles: the 8 rows of a k-step are contiguous).
-      // Product j = (head-dim tile j / (2 MT), k-step j % (2 MT)); operands through rings.
-      constexpr int NJ = NDH * 2 * MT;
-      auto aread = [&](const bf16_t* base, int j) {
-        return lds_read_b128(base + (32 * (j / (2 * MT)) + l32) * TSTR + 8 * hh + 16 * (j % (2 * MT)));
-      };
-      bf16x8 ao[kRing], aq[kRing];
+      // dV^T += dO^T P and dK^T += Q^T dS (A operands from the transposed tiles: the 8 rows
+      // of a k-step are contiguous).
+      if constexpr (kAcc) operands_ready(pP[0], pS[0]);
 #pragma unroll
-      for (int i = 0; i < kAh; ++i) {
+      for (int i = 1; i < kAh; ++i) {
         ao[i] = aread(sOT, i);
         aq[i] = aread(sQT, i);
       }
@@ -391,8 +423,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
           aq[(j + kAh) % kRing] = aread(sQT, j + kAh);
         }
         const int dt = j / (2 * MT), kstep = j % (2 * MT);
-        dv[dt] = mfma32(ao[j % kRing], pP[kstep >> 1][kstep & 1], dv[dt]);
-        dk[dt] = mfma32(aq[j % kRing], pS[kstep >> 1][kstep & 1], dk[dt]);
+        if constexpr (kAcc) {
+          mfma_acc(dv[dt], ao[j % kRing], pP[kstep >> 1][kstep & 1]);
+          mfma_acc(dk[dt], aq[j % kRing], pS[kstep >> 1][kstep & 1]);
+        } else {
+          dv[dt] = mfma32(ao[j % kRing], pP[kstep >> 1][kstep & 1], dv[dt]);
+          dk[dt] = mfma32(aq[j % kRing], pS[kstep >> 1][kstep & 1], dk[dt]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -403,9 +440,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     __syncthreads();
   }
 
+  if constexpr (kAcc) {
+    acc_ready(dk);
+    acc_ready(dv);
+  }
   if (key < N) {
-    bf16_t* dkr = dK + ((size_t)seq0 + key) * ks + (size_t)hkv * D + dh0;
-    bf16_t* dvr = dV + ((size_t)seq0 + key) * ks + (size_t)hkv * D + dh0;
+    bf16_t* dkr = dK + ((size_t)seq0 + key) * ks + (size_t)hkv * D;
+    bf16_t* dvr = dV + ((size_t)seq0 + key) * ks + (size_t)hkv * D;
 #pragma unroll
     for (int dt = 0; dt < NDH; ++dt) {
 #pragma unroll
@@ -1051,11 +1092,13 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
   constexpr bool kWide = D <= 128;  // 8-wave key-block kernel
   // Dynamic LDS limits, set once (a function-local static: the first call is thread-safe).
   static const hipError_t attr = [] {
-    const hipError_t e =
-        kWide ? hipFuncSetAttribute((const void*)bwd_dkdv8_kernel<D <= 128 ? D : 128, AL>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, K8::LDS_BYTES)
-              : hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, AL>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, KC::LDS_BYTES);
+    hipError_t e;
+    if constexpr (kWide)
+      e = hipFuncSetAttribute((const void*)bwd_dkdv8_kernel<D, AL>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, K8::LDS_BYTES);
+    else
+      e = hipFuncSetAttribute((const void*)bwd_dkdv_kernel<D, AL>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, KC::LDS_BYTES);
     if (e != hipSuccess) return e;
     return hipFuncSetAttribute((const void*)bwd_dq_kernel<D, AL>,
                                hipFuncAttributeMaxDynamicSharedMemorySize, QC::LDS_BYTES);
@@ -1082,7 +1125,7 @@ static hipError_t launch_bwd_d(const BwdArgs& a, hipStream_t st) {
                        a.c_log2_signed, a.scale, a.cu, a.ntot, a.slopes);
   } else {
     const int num_kb = (a.N + KC::BKN - 1) / KC::BKN;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, AL>), dim3(a.B * a.Hkv * num_kb * KC::NSPLIT),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, AL>), dim3(a.B * a.Hkv * num_kb),
                        dim3(KC::NT), KC::LDS_BYTES, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
                        (const bf16_t*)a.v, (const bf16_t*)a.dO, a.lse, a.dvec, (bf16_t*)a.dk,
                        (bf16_t*)a.dv, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window,
