@@ -1,5 +1,8 @@
 """Build checks on the CPU (hipcc cross-compiles for gfx950 without a GPU).
 
+The last check reads the generated assembly of the head-dim-256 key-block kernel, whose
+dK/dV products are inline assembly with hand-written wait states (see there).
+
 No kernel may use scratch memory (register spills to memory inside an inner loop cost more
 than the changes that would cause one save).  The kernels for head dims 64 and 128 must
 also compile without any vector-register spill; the head-dim-256 kernels run one wave per
@@ -82,3 +85,79 @@ def test_head_dim_256_kernels_are_covered(usage):
     names = " ".join(n for n in usage if "ILi256E" in n)
     for k in ("fwd_bf16_kernel", "fwd_fp8_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
         assert k in names, k
+
+
+# The head-dim-256 key-block kernel accumulates dK and dV in AGPRs through matrix products
+# written as inline assembly; the compiler does not see them as matrix instructions, so the
+# wait states around them are written out in the source.  These checks read the generated
+# gfx950 assembly and pin what those waits rely on: the accumulators are touched by vector
+# instructions only before the first product (zeroing, then the short fence) and after the
+# long fence that follows the last one, and nothing moves them inside the step loop.
+ASM_PRODUCT = re.compile(r"v_mfma_f32_32x32x16_bf16 a\[(\d+):(\d+)\], v\[\d+:\d+\], "
+                         r"v\[\d+:\d+\], a\[(\d+):(\d+)\]")
+
+
+@pytest.fixture(scope="module")
+def bwd_asm():
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as tmpdir:
+        out = os.path.join(tmpdir, "fa_bwd.s")
+        cmd = ([B.hipcc()] + B.HIPCC_FLAGS + B.FILE_FLAGS.get("fa_bwd.hip", []) +
+               ["--cuda-device-only", "-S", os.path.join(B.CSRC, "fa_bwd.hip"), "-o", out])
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-2000:]
+        with open(out) as f:
+            return f.read()
+
+
+def _function_bodies(asm: str, prefix: str) -> dict:
+    lines = asm.splitlines()
+    bodies, i = {}, 0
+    while i < len(lines):
+        if lines[i].startswith(prefix) and lines[i].split(":")[0] == lines[i].split()[0][:-1]:
+            name = lines[i].split(":")[0]
+            j = next(k for k in range(i, len(lines)) if lines[k].startswith(".Lfunc_end"))
+            bodies[name] = [l.strip() for l in lines[i:j]]
+            i = j
+        i += 1
+    return bodies
+
+
+def _asm_blocks(body: list) -> list:
+    """(line index, text) of every inline-assembly block of a function body."""
+    out, i = [], 0
+    while i < len(body):
+        if body[i].startswith(";;#ASMSTART"):
+            j = i + 1
+            while not body[j].startswith(";;#ASMEND"):
+                j += 1
+            out.append((i, "\n".join(body[i + 1:j])))
+            i = j
+        i += 1
+    return out
+
+
+def test_head_dim_256_key_block_kernel_fences_its_agpr_products(bwd_asm):
+    bodies = _function_bodies(bwd_asm, "_ZN2fa15bwd_dkdv_kernelILi256E")
+    assert len(bodies) == 3, list(bodies)  # unbiased, causal and general position bias
+    for name, body in bodies.items():
+        blocks = _asm_blocks(body)
+        products = [(i, t) for i, t in blocks if "v_mfma" in t]
+        # 8 head-dim tiles x 2 k-steps x (dV, dK) per step, unrolled
+        assert len(products) == 32, (name, len(products))
+        for _, t in products:
+            m = ASM_PRODUCT.search(t)
+            assert m and m.group(1, 2) == m.group(3, 4), (name, t)  # acc += a b in AGPRs
+        written = [i for i, t in blocks if t.strip() == "s_nop 4"]
+        ready = [i for i, t in blocks if t.split() == ["s_nop", "7", "s_nop", "7", "s_nop", "7"]]
+        assert len(written) == 2 and len(ready) == 2, (name, len(written), len(ready))
+        first, last = products[0][0], products[-1][0]
+        assert max(written) < first < last < min(ready), name
+        acc_moves = [i for i, l in enumerate(body) if l.startswith("v_accvgpr_")]
+        between = [i for i in acc_moves if first < i < max(ready)]
+        assert not between, (name, [body[i] for i in between][:4])
+        reads = [i for i in acc_moves if body[i].startswith("v_accvgpr_read")]
+        assert reads and min(reads) > max(ready), name
+        writes = [i for i in acc_moves if not body[i].startswith("v_accvgpr_read")]
+        assert writes and max(writes) < min(written), name
