@@ -143,6 +143,20 @@ __device__ __forceinline__ void operands_ready(bf16x8 (&p)[2], bf16x8 (&q)[2]) {
   asm volatile("s_nop 1" : "+v"(p[0]), "+v"(p[1]), "+v"(q[0]), "+v"(q[1]));
 }
 
+// Order of the (4-row group, 8-column chunk) staging tasks of the d = 256 kernels: lane bits
+// 0-1 pick the chunk, bits 2-3 the row group, higher bits the rest.  The LDS has 32
+// four-byte banks for stores and writes 8 lanes of a 16-byte store per cycle; with row
+// strides of 4 (mod 32) dwords the 8 lanes of a row-major store then cover two row groups
+// and four chunks, 32 distinct banks, where task_rc's four row groups put two lanes on
+// every bank.  The transposed stores (16 lanes per cycle, four row groups) are as before.
+// A bijection on [0, rows / 4 * CPR) when rows is a multiple of 16 and CPR of 4.
+template <int CPR>
+__device__ __forceinline__ void task_rc4(int t, int& rg, int& dc) {
+  const int q = t >> 4;
+  dc = (t & 3) + 4 * (q % (CPR / 4));
+  rg = ((t >> 2) & 3) + 4 * (q / (CPR / 4));
+}
+
 template <int D>
 struct KVCfg {
   static constexpr int NT = 256;                 // 4 waves x 32 keys
@@ -231,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   // Staging: a task = 4 rows x 8 dims of Q and of dO, stored row-major and transposed.
   constexpr int CPR = D / 8;
   constexpr int TASKS = (BQ / 4) * CPR;
-  static_assert(BQ % 16 == 0, "task_rc needs whole groups of 16 rows");
+  static_assert(BQ % 16 == 0 && CPR % 4 == 0, "task_rc4 needs whole groups of 16 rows and 4 chunks");
   constexpr int PT = (TASKS + 255) / 256;
   uint4 qr[PT][4], orr[PT][4];
   float lreg = 0.f, dreg = 0.f;
@@ -248,7 +262,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       const int task = tid + 256 * p;
       if (TASKS % 256 == 0 || task < TASKS) {
         int rg, dc;
-        task_rc<CPR>(task, rg, dc);
+        task_rc4<CPR>(task, rg, dc);
         const uint32_t off = (uint32_t)(4 * rg * qs + 8 * dc) * 2u;
         bload_4x8(qr[p], qres, off, (uint32_t)qs * 2u);
         bload_4x8(orr[p], ores, off, (uint32_t)qs * 2u);
@@ -272,7 +286,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       const int task = tid + 256 * p;
       if (TASKS % 256 == 0 || task < TASKS) {
         int rg, dc;
-        task_rc<CPR>(task, rg, dc);
+        task_rc4<CPR>(task, rg, dc);
         store_4x8_rows(sQ, STR, 4 * rg, 8 * dc, qr[p]);
         store_4x8_rows(sO, STR, 4 * rg, 8 * dc, orr[p]);
         store_4x8_transposed(sQT, TSTR, 4 * rg, 8 * dc, qr[p]);
@@ -855,7 +869,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   constexpr int TP = (BN / 2) * CPR;  // 2-key tasks per operand
   static_assert(!kPairs || TP <= NT, "one 2-key task of K and of V per thread");
   constexpr int TK = (BN / 4) * CPR;
-  static_assert(BN % 16 == 0, "task_rc needs whole groups of 16 rows");
+  static_assert(BN % 16 == 0 && CPR % 4 == 0, "task_rc4 needs whole groups of 16 rows and 4 chunks");
   constexpr int PT = kPairs ? 1 : (2 * TK + NT - 1) / NT;
   static_assert(kPairs || TK % 64 == 0, "K and V tasks fall on whole waves");
   uint4 xr[PT][4];
@@ -882,7 +896,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
           const bool isv = wtask >= TK;  // wave-uniform, keeps the buffer resource scalar
           const int t = isv ? task - TK : task;
           int kg, dc;
-          task_rc<CPR>(t, kg, dc);
+          task_rc4<CPR>(t, kg, dc);
           const rsrc_t res = make_rsrc((isv ? Vh : Kh) + (size_t)nb * BN * ks, bytes);
           bload_4x8(xr[p], res, (uint32_t)(4 * kg * ks + 8 * dc) * 2u, (uint32_t)ks * 2u);
         }
@@ -918,7 +932,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
           const bool isv = task >= TK;
           const int t = isv ? task - TK : task;
           int kg, dc;
-          task_rc<CPR>(t, kg, dc);
+          task_rc4<CPR>(t, kg, dc);
           if (isv) {
             store_4x8_rows(sV, KSTR, 4 * kg, 8 * dc, xr[p]);
           } else {
