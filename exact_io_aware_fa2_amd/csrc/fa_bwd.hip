@@ -571,9 +571,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
 
   // Staging tasks of a step: 2 rows x 8 dims each, [0, T2) of Q and [T2, 2 T2) of dO, one
   // per thread, so all eight waves share the staging; each is stored row-major and
-  // transposed.  Row pairs run fastest inside a wave: the row-major 16-byte stores of 8
-  // neighbouring lanes then hit distinct banks and the transposed 4-byte stores of 16
-  // neighbouring lanes fill one 64-byte run of a transposed row.
+  // transposed.  Lane bit 0 picks one of two chunks, the next bits the row pair: the 8
+  // lanes the LDS writes per cycle of a 16-byte store (32 four-byte banks) then cover four
+  // row pairs and two chunks, 32 distinct banks, where eight row pairs of one chunk (row
+  // stride 4 dwords mod 32) put two lanes on every bank; the transposed 4-byte stores are
+  // two-way either way (16 row pairs per transposed row, chunks 8 rows = 0 banks apart).
   constexpr int CPR = D / 8;
   constexpr int T2 = (BQ / 2) * CPR;
   static_assert(2 * T2 <= NT, "one staging task per thread");
@@ -581,7 +583,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv8_kernel(
   // Which operand a wave stages is wave-uniform, so its buffer resource stays scalar.
   const bool stager = w < 2 * T2 / 64, iso = w >= T2 / 64;
   const int tt = iso ? tid - T2 : tid;
-  const int rp = tt % (BQ / 2), dc = tt / (BQ / 2);  // row pair, 8-dim chunk
+  const int rp = (tt >> 1) % (BQ / 2), dc = (tt & 1) + 2 * (tt / BQ);  // row pair, chunk
   // Every thread fetches the LSE / D value of row tid % BQ of the step, unconditionally and
   // unscaled: a load consumed only at the next step's LDS write must not sit on a branch
   // merge or feed arithmetic right away, or the wait for it lands right behind its issue.
@@ -861,8 +863,12 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   const int khi = causal ? min(row, N - 1) : N - 1;
 
   // Staging.  d <= 128: every thread takes one 2-key x 8-dim task of K (stored row-major
-  // and transposed) and the same task of V (row-major), key pairs fastest inside a wave,
-  // so the work is even over the waves and the stores are free of bank conflicts.
+  // and transposed) and the same task of V (row-major), so the work is even over the
+  // waves.  Lane bit 0 picks one of two chunks, the next bits the key pair: the 8 lanes the
+  // LDS writes per cycle of a 16-byte store (32 four-byte banks) then cover four key pairs
+  // and two chunks, 32 distinct banks (eight key pairs of one chunk would put two lanes on
+  // every bank), at the price of two-way 4-byte K^T stores (16 key pairs per cycle instead
+  // of 32); the row-major stores are four per task, the transposed ones eight 4-byte ones.
   // d = 256: 4-key x 8-dim tasks, [0, TK) of K and [TK, 2 TK) of V.
   constexpr int CPR = D / 8;
   constexpr bool kPairs = D <= 128;
@@ -873,7 +879,7 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
   constexpr int PT = kPairs ? 1 : (2 * TK + NT - 1) / NT;
   static_assert(kPairs || TK % 64 == 0, "K and V tasks fall on whole waves");
   uint4 xr[PT][4];
-  const int kp_ = tid % (BN / 2), dcp = tid / (BN / 2);  // key pair, 8-dim chunk
+  const int kp_ = (tid >> 1) % (BN / 2), dcp = (tid & 1) + 2 * (tid / BN);  // key pair, chunk
   const bool ptask = TP == NT || tid < TP;
   auto gload = [&](int nb) {
     const uint32_t bytes = (uint32_t)(N - nb * BN) * (uint32_t)ks * 2u;  // rows past N read 0
