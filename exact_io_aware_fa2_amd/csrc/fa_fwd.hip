@@ -121,7 +121,15 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   constexpr int KCH = BN * CPR;           // K chunks per tile (d = 256)
   constexpr int PTK = kPairs ? 1 : (KCH + NT - 1) / NT;
   constexpr int VTASKS = (BN / 4) * CPR;  // (4-key group, 8-dim chunk) tasks (d = 256)
-  static_assert(BN % 16 == 0, "task_rc needs whole groups of 16 keys");
+  // V task t = (4-key group t % (BN / 4), chunk t / (BN / 4)): key groups fastest, so the
+  // 16 lanes the LDS writes per cycle of an 8-byte transposed store (32 four-byte banks)
+  // span all eight key groups of a 32-key tile and two chunks, two lanes per bank (the
+  // chunks' rows lie a multiple of 32 banks apart), instead of four groups and four chunks,
+  // four per bank.
+  auto vtask = [](int t, int& kg, int& dc) {
+    kg = t % (BN / 4);
+    dc = t / (BN / 4);
+  };
   constexpr int PTV = kPairs ? 1 : (VTASKS + NT - 1) / NT;
   const uint32_t row_bytes = (uint32_t)ks * 2u;
   // d <= 128
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int p = 0; p < PTV; ++p) {
       int kg, dc;
-      task_rc<CPR>(tid + NT * p, kg, dc);
+      vtask(tid + NT * p, kg, dc);
       voff[p] = (uint32_t)(4 * kg * ks + dc * 8) * 2u;
     }
   }
@@ -203,7 +211,7 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
         const int task = tid + NT * p;
         if (VTASKS % NT == 0 || task < VTASKS) {
           int kg, dc;
-          task_rc<CPR>(task, kg, dc);
+          vtask(task, kg, dc);
           bf16_t* dst = sV + (dc * 8) * VSTR + vt_pos(4 * kg);
 #pragma unroll
           for (int m = 0; m < 4; ++m) {
