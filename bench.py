@@ -138,6 +138,28 @@ def issue_probe(fa, torch, dev, stream, iters: int = 4000, reps: int = 3):
     return res
 
 
+LDS_PROBE_STRIDES = (4, 8, 16, 32, 64, 128, 256)
+
+
+def lds_probe(fa, torch, dev, stream, iters: int = 2000):
+    """Launch the LDS bank probes of fa_issue_probe (kinds 4 and 5) once each, one workgroup
+    per CU, in the order returned; the bank-conflict counters of these launches (rocprofv3
+    --pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS) give cycles per access."""
+    blocks = 256
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    sh = stream.cuda_stream
+    launches = []
+    for kind, access in ((4, "store"), (5, "load")):
+        for width in (4, 8, 16):
+            for stride in LDS_PROBE_STRIDES:
+                if fa.fa_issue_probe(out, kind, width * 10000 + stride, 1, blocks, iters, sh) != fa.FA_OK:
+                    raise RuntimeError(fa.fa_last_error())
+                launches.append({"access": access, "width_bytes": width, "stride_bytes": stride})
+    torch.cuda.synchronize()
+    return {"launches_in_order": launches, "workgroups": blocks, "waves_per_workgroup": 4,
+            "iters": iters}
+
+
 def atomic_dq_count(w, bkn: int = 256, bq: int = 32) -> int:
     """float32 atomic adds an atomic accumulation of dQ would issue for a fixed-length
     workload: every key block of `bkn` keys adds, for each 32-row step it visits (the same
@@ -386,6 +408,8 @@ def run_decode(args, w):
     }
     if args.probe_issue:
         out["issue_probe_frac_of_peak"] = issue_probe(fa, torch, dev, stream)
+    if args.probe_lds:
+        out["lds_probe"] = lds_probe(fa, torch, dev, stream)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -414,6 +438,9 @@ def main() -> int:
     ap.add_argument("--probe-issue", action="store_true",
                     help="also run the fa_issue_probe table: matrix-core throughput next to "
                          "FMAs, exp2, LDS operand reads, and over dependent chains")
+    ap.add_argument("--probe-lds", action="store_true",
+                    help="also launch the LDS bank probes (store and load, 4/8/16 bytes per "
+                         "lane, strides 4-256 bytes) for a rocprofv3 counter run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a known-size kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
@@ -624,6 +651,8 @@ def main() -> int:
                     "and a zeroing and a conversion pass of the float32 accumulator"}
     if args.probe_issue:
         out["issue_probe_frac_of_peak"] = issue_probe(fa, torch, dev, stream)
+    if args.probe_lds:
+        out["lds_probe"] = lds_probe(fa, torch, dev, stream)
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)

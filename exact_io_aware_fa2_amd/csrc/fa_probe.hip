@@ -8,6 +8,9 @@
 //   * issue probes: matrix products next to the other work the attention kernels put
 //     beside them (FMAs, exp2, LDS operand reads) and dependent product chains, to measure
 //     how much of that work the matrix core's issue pattern leaves room for.
+//   * LDS bank probes: every lane of a wave stores to (or loads from) LDS at lane * stride
+//     bytes, so the bank-conflict counters of the launch give the bank count and the lanes
+//     served per cycle for each access width (the layouts of the staged tiles rest on them);
 //   * a kernel that runs single 32 x 32 x 64 products of 8-bit E4M3 operands given by the
 //     caller, so the accuracy of the 8-bit matrix core's 64-term sums can be checked
 //     against exact sums (the error bound the 8-bit forward's tolerances rest on).
@@ -213,6 +216,49 @@ __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out,
   out[blockIdx.x * blockDim.x + t] = s;
 }
 
+// LDS bank probe: every wave of the workgroup accesses 64 KiB of LDS at lane * stride
+// bytes (masked to the array and aligned to the access width) `iters` times, with a
+// compiler barrier between rounds so every access is issued; W bytes per access.
+template <int W, bool STORE>
+__global__ __launch_bounds__(512) void lds_bank_kernel(float* __restrict__ out, int stride,
+                                                       int iters) {
+  __shared__ __attribute__((aligned(16))) uint32_t buf[16384];
+  const int t = threadIdx.x, lane = t & 63;
+  for (int i = t; i < 16384; i += blockDim.x) buf[i] = i;
+  __syncthreads();
+  char* base = reinterpret_cast<char*>(buf);
+  const uint32_t a = ((uint32_t)lane * (uint32_t)stride) & (65536u - W);
+  uint32_t acc = 0;
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (STORE) {
+      if constexpr (W == 4) *reinterpret_cast<uint32_t*>(base + a) = it;
+      if constexpr (W == 8) *reinterpret_cast<uint2*>(base + a) = make_uint2(it, t);
+      if constexpr (W == 16) *reinterpret_cast<uint4*>(base + a) = make_uint4(it, t, it, t);
+    } else {
+      if constexpr (W == 4) acc ^= *reinterpret_cast<const uint32_t*>(base + a);
+      if constexpr (W == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(base + a);
+        acc ^= v.x ^ v.y;
+      }
+      if constexpr (W == 16) {
+        const uint4 v = *reinterpret_cast<const uint4*>(base + a);
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+  __syncthreads();
+  out[blockIdx.x * blockDim.x + t] = __uint_as_float(acc ^ buf[(t * 17) & 16383]);
+}
+
+template <int W, bool STORE>
+static hipError_t launch_lds_bank(int blocks, int threads, float* out, int stride, int iters,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL((lds_bank_kernel<W, STORE>), dim3(blocks), dim3(threads), 0, st, out,
+                     stride, iters);
+  return hipGetLastError();
+}
+
 template <typename Kernel>
 static hipError_t launch_issue(Kernel k, int blocks, int threads, size_t lds, float* out,
                                int iters, hipStream_t st) {
@@ -228,6 +274,19 @@ static hipError_t launch_issue(Kernel k, int blocks, int threads, size_t lds, fl
 hipError_t launch_issue_probe(float* out, int kind, int param, int waves_per_simd, int blocks,
                               int iters, hipStream_t st) {
   const int threads = 256 * waves_per_simd;
+  if (kind == 4 || kind == 5) {  // LDS bank probe: param = width * 10000 + stride
+    const int width = param / 10000, stride = param % 10000;
+    const bool store = kind == 4;
+    switch (width * 2 + (store ? 1 : 0)) {
+      case 9: return launch_lds_bank<4, true>(blocks, threads, out, stride, iters, st);
+      case 8: return launch_lds_bank<4, false>(blocks, threads, out, stride, iters, st);
+      case 17: return launch_lds_bank<8, true>(blocks, threads, out, stride, iters, st);
+      case 16: return launch_lds_bank<8, false>(blocks, threads, out, stride, iters, st);
+      case 33: return launch_lds_bank<16, true>(blocks, threads, out, stride, iters, st);
+      case 32: return launch_lds_bank<16, false>(blocks, threads, out, stride, iters, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (kind * 100 + param) {
     case 0: return launch_issue(issue_valu_kernel<0, false>, blocks, threads, 0, out, iters, st);
     case 2: return launch_issue(issue_valu_kernel<2, false>, blocks, threads, 0, out, iters, st);

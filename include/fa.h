@@ -305,6 +305,12 @@ fa_status fa_atomic_probe(float* acc, int row_blocks, int stride, int blocks, in
  *   3  param in {0,1,2}:        param operands of each product read from LDS (16 bytes per
  *                               lane, one round ahead; 64 KiB of LDS per workgroup; iters
  *                               is rounded up to an even count).
+ *   4, 5  param = width * 10000 + stride, width in {4,8,16} bytes, stride in [1, 4096]:
+ *                               no products; every wave stores (4) or loads (5) `width`
+ *                               bytes per lane at LDS byte lane * stride (masked to 64 KiB
+ *                               and aligned down to the width), `iters` times, so the LDS
+ *                               bank-conflict counters of the launch measure the banks and
+ *                               the lanes served per cycle at that width.
  * The caller times the launch.  FA_ERR_UNSUPPORTED for another (kind, param),
  * FA_ERR_INVALID_ARG for a null pointer, waves_per_simd not 1 or 2, or non-positive counts.
  */
