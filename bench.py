@@ -588,8 +588,9 @@ def main() -> int:
     out["fwd_tflops"] = F / (fwd_avg * 1e-3) / 1e12
     peak = MFMA_FP8_PEAK_TFLOPS if fp8 else MFMA_BF16_PEAK_TFLOPS
     out["fwd_frac_of_peak"] = out["fwd_tflops"] / peak
-    kernels = ({"fwd_fp8_kernel": (fwd_avg, F, "fa_fwd_fp8.hip")} if fp8 else
-               {"fwd_bf16_kernel": (fwd_avg, F, "fa_fwd.hip")})
+    fwd_name = ("fwd_fp8_kernel" if fp8 else
+                "fwd_bf16_kernel" if w.d <= 128 else "fwd_bf16_d256_kernel")
+    kernels = {fwd_name: (fwd_avg, F, "fa_fwd_fp8.hip" if fp8 else "fa_fwd.hip")}
     if bwd:
         bwd_ms = [e[2].elapsed_time(e[3]) for e in ev]
         pre_ms = [e[2].elapsed_time(e[4]) for e in ev]   # D = rowsum(dO * O)

@@ -48,6 +48,31 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Matrix products whose accumulators live in AGPRs.  The compiler gives a kernel either
+// every product in the AGPR form or none, and the d = 256 kernels need their accumulators
+// (dK/dV, or O) in AGPRs next to VGPR scores, so those products are inline assembly.  The
+// compiler does not see them as matrix instructions: the wait states the hardware needs
+// where vector instructions touch their registers are written out here.
+// acc += a b (v_mfma_f32_32x32x16_bf16 with an AGPR accumulator).
+__device__ __forceinline__ void mfma_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// After vector writes of accumulators, before a product reads them.
+__device__ __forceinline__ void acc_written(f32x16 (&x)[8]) {
+  asm volatile("s_nop 4"
+               : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]),
+                 "+a"(x[6]), "+a"(x[7]));
+}
+// After the last product, before vector instructions read the accumulators (more wait
+// states than a 32x32x16 product's latency).
+__device__ __forceinline__ void acc_ready(f32x16 (&x)[8]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]),
+                 "+a"(x[6]), "+a"(x[7]));
+}
+// After vector writes of a product operand, before the products read it.
+__device__ __forceinline__ void operand_ready(bf16x8& p) { asm volatile("s_nop 1" : "+v"(p)); }
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll

@@ -6,12 +6,12 @@
 // denominator kept apart and combined once at the end; section 3.2: the Q tile stays in
 // registers while K and V tiles go through shared memory).
 //
-// bf16 kernel, one workgroup = 8 waves = 256 query rows (d <= 128; 4 waves = 128 rows for
-// d = 256) of one (batch entry, query head):
+// bf16 kernel for d <= 128, one workgroup = 8 waves = 256 query rows of one (batch entry,
+// query head) (d = 256: fwd_bf16_d256_kernel below):
 //   * each wave owns 32 query rows; its Q rows sit in VGPRs as the B operand of
 //     S^T = K Q^T (32 keys x 32 rows per MFMA tile), so every lane holds one query row
 //     and 16 of its scores per tile -> row max/sum need one cross-half exchange only;
-//   * K and V tiles (64 keys for d <= 128) are staged in LDS, double-buffered, from
+//   * K and V tiles of 64 keys are staged in LDS, double-buffered, from
 //     16-byte raw buffer loads issued one tile ahead; V is transposed on the way in
 //     (v_perm_b32 on register pairs), so V^T rows are plain 16-byte LDS reads;
 //   * P^T (the accumulator of S^T after exp2) feeds O^T += V^T P^T directly as the B
@@ -29,10 +29,11 @@ namespace fa {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int NW = D <= 128 ? 8 : 4;  // waves per workgroup (2 or 1 per SIMD)
+  static_assert(D <= 128, "head dim 256 has its own kernel");
+  static constexpr int NW = 8;                 // waves per workgroup (2 per SIMD)
   static constexpr int NT = 64 * NW;           // threads per workgroup
   static constexpr int BM = 32 * NW;           // query rows per workgroup (32 per wave)
-  static constexpr int BN = D <= 128 ? 64 : 32;  // keys staged per iteration
+  static constexpr int BN = 64;                // keys staged per iteration
   static constexpr int KSTR = D + 8;           // K tile row stride in elements (16-byte pad)
   static constexpr int VSTR = BN + 8;          // V^T tile row stride in elements (16-byte pad)
   static constexpr int K_ELEMS = BN * KSTR;
@@ -60,8 +61,6 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   constexpr int NT = Cfg::NT, BM = Cfg::BM, BN = Cfg::BN, KSTR = Cfg::KSTR, VSTR = Cfg::VSTR;
   constexpr int NC = D / 16;  // k-steps of S^T over the head dim
   constexpr int ND = D / 32;  // 32-wide head-dim tiles of O^T
-  constexpr bool kStream = D > 128;   // K / V^T operands streamed (see the piece loop)
-  constexpr int kRing = 4, kAhead = 3;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
 
@@ -107,125 +106,45 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
   if (window > 0) kv_lo = max(0, m0 - window + 1);
   const int nb_lo = kv_lo / BN, nb_hi = (kv_hi + BN - 1) / BN;
 
-  // Staging.  d <= 128 (64-key tiles, 512 threads): thread = (key pair kp, 8-dim chunk dcp)
-  // of K and of V, K stored row-major and V transposed (16-bit lane packing, one 32-bit
-  // word per V^T row), the same work for every thread; key pairs run fastest inside a
-  // wave, which keeps both kinds of store free of bank conflicts.  d = 256 (32-key tiles,
-  // 256 threads): K rows as 16-byte chunks, V as 4 keys x 8 dims per task, transposed in
-  // registers.  Tiles are read through buffer resources whose size ends at row N, so rows
-  // past the end of the sequence load as zeros.
+  // Staging (64-key tiles, 512 threads): thread = (key pair kp, 8-dim chunk dcp) of K and
+  // of V, K stored row-major and V transposed (16-bit lane packing, one 32-bit word per V^T
+  // row), the same work for every thread; key pairs run fastest inside a wave, which keeps
+  // both kinds of store free of bank conflicts.  Tiles are read through buffer resources
+  // whose size ends at row N, so rows past the end of the sequence load as zeros.
   constexpr int CPR = D / 8;              // 16-byte chunks per K/V row
-  constexpr bool kPairs = D <= 128;
-  constexpr int TP = (BN / 2) * CPR;      // key-pair tasks per tile (d <= 128)
-  static_assert(!kPairs || TP <= NT, "one key-pair task per thread");
-  constexpr int KCH = BN * CPR;           // K chunks per tile (d = 256)
-  constexpr int PTK = kPairs ? 1 : (KCH + NT - 1) / NT;
-  constexpr int VTASKS = (BN / 4) * CPR;  // (4-key group, 8-dim chunk) tasks (d = 256)
-  // V task t = (4-key group t % (BN / 4), chunk t / (BN / 4)): key groups fastest, so the
-  // 16 lanes the LDS writes per cycle of an 8-byte transposed store (32 four-byte banks)
-  // span all eight key groups of a 32-key tile and two chunks, two lanes per bank (the
-  // chunks' rows lie a multiple of 32 banks apart), instead of four groups and four chunks,
-  // four per bank.
-  auto vtask = [](int t, int& kg, int& dc) {
-    kg = t % (BN / 4);
-    dc = t / (BN / 4);
-  };
-  constexpr int PTV = kPairs ? 1 : (VTASKS + NT - 1) / NT;
+  constexpr int TP = (BN / 2) * CPR;      // key-pair tasks per tile
+  static_assert(TP <= NT, "one key-pair task per thread");
   const uint32_t row_bytes = (uint32_t)ks * 2u;
-  // d <= 128
   const bool ptask = TP == NT || tid < TP;
   const int kp = tid % (BN / 2), dcp = tid / (BN / 2);
   const uint32_t poff = (uint32_t)(2 * kp * ks + 8 * dcp) * 2u;
   uint4 xk[2], xv[2];
-  // d = 256
-  uint4 kr[PTK], vr[PTV][4];
-  uint32_t koff[PTK], voff[PTV];
-  if constexpr (!kPairs) {
-#pragma unroll
-    for (int i = 0; i < PTK; ++i) {
-      const int ch = tid + NT * i;
-      const int key = ch / CPR, dc = ch - key * CPR;
-      koff[i] = (uint32_t)(key * ks + dc * 8) * 2u;
-    }
-#pragma unroll
-    for (int p = 0; p < PTV; ++p) {
-      int kg, dc;
-      vtask(tid + NT * p, kg, dc);
-      voff[p] = (uint32_t)(4 * kg * ks + dc * 8) * 2u;
-    }
-  }
   auto gload = [&](int nb) {
     const int n0 = nb * BN;
     const uint32_t bytes = (uint32_t)(N - n0) * row_bytes;
     const rsrc_t kres = make_rsrc(Kh + (size_t)n0 * ks, bytes);
     const rsrc_t vres = make_rsrc(Vh + (size_t)n0 * ks, bytes);
-    if constexpr (kPairs) {
-      if (ptask) {
-        xk[0] = bload16(kres, poff);
-        xk[1] = bload16(kres, poff + row_bytes);
-        xv[0] = bload16(vres, poff);
-        xv[1] = bload16(vres, poff + row_bytes);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PTK; ++i) {
-        if (KCH % NT == 0 || tid + NT * i < KCH) kr[i] = bload16(kres, koff[i]);
-      }
-#pragma unroll
-      for (int p = 0; p < PTV; ++p) {
-        if (VTASKS % NT == 0 || tid + NT * p < VTASKS) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vr[p][e] = bload16(vres, voff[p] + e * row_bytes);
-        }
-      }
+    if (ptask) {
+      xk[0] = bload16(kres, poff);
+      xk[1] = bload16(kres, poff + row_bytes);
+      xv[0] = bload16(vres, poff);
+      xv[1] = bload16(vres, poff + row_bytes);
     }
   };
   auto swrite = [&](int buf) {
     bf16_t* sK = lds + buf * Cfg::BUF_ELEMS;
     bf16_t* sV = sK + Cfg::K_ELEMS;
-    if constexpr (kPairs) {
-      if (ptask) {
-        bf16_t* kd = sK + (2 * kp) * KSTR + 8 * dcp;
-        *reinterpret_cast<uint4*>(kd) = xk[0];
-        *reinterpret_cast<uint4*>(kd + KSTR) = xk[1];
-        // dim 8 dcp + j of the two keys -> one 32-bit word of V^T row 8 dcp + j
-        bf16_t* vd = sV + (8 * dcp) * VSTR + vt_pos(2 * kp);
+    if (ptask) {
+      bf16_t* kd = sK + (2 * kp) * KSTR + 8 * dcp;
+      *reinterpret_cast<uint4*>(kd) = xk[0];
+      *reinterpret_cast<uint4*>(kd + KSTR) = xk[1];
+      // dim 8 dcp + j of the two keys -> one 32-bit word of V^T row 8 dcp + j
+      bf16_t* vd = sV + (8 * dcp) * VSTR + vt_pos(2 * kp);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const uint32_t a0 = word(xv[0], m), a1 = word(xv[1], m);
-          *reinterpret_cast<uint32_t*>(vd + (2 * m) * VSTR) = pack_lo(a0, a1);
-          *reinterpret_cast<uint32_t*>(vd + (2 * m + 1) * VSTR) = pack_hi(a0, a1);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < PTK; ++i) {
-        const int ch = tid + NT * i;
-        if (KCH % NT == 0 || ch < KCH) {
-          const int key = ch / CPR, dc = ch - key * CPR;
-          *reinterpret_cast<uint4*>(sK + key * KSTR + dc * 8) = kr[i];
-        }
-      }
-#pragma unroll
-      for (int p = 0; p < PTV; ++p) {
-        const int task = tid + NT * p;
-        if (VTASKS % NT == 0 || task < VTASKS) {
-          int kg, dc;
-          vtask(task, kg, dc);
-          bf16_t* dst = sV + (dc * 8) * VSTR + vt_pos(4 * kg);
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint32_t a0 = word(vr[p][0], m), a1 = word(vr[p][1], m);
-            const uint32_t a2 = word(vr[p][2], m), a3 = word(vr[p][3], m);
-            uint2 even, odd;  // dims 2m and 2m+1, keys 0..3 of the group
-            even.x = pack_lo(a0, a1);
-            even.y = pack_lo(a2, a3);
-            odd.x = pack_hi(a0, a1);
-            odd.y = pack_hi(a2, a3);
-            *reinterpret_cast<uint2*>(dst + (2 * m) * VSTR) = even;
-            *reinterpret_cast<uint2*>(dst + (2 * m + 1) * VSTR) = odd;
-          }
-        }
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t a0 = word(xv[0], m), a1 = word(xv[1], m);
+        *reinterpret_cast<uint32_t*>(vd + (2 * m) * VSTR) = pack_lo(a0, a1);
+        *reinterpret_cast<uint32_t*>(vd + (2 * m + 1) * VSTR) = pack_hi(a0, a1);
       }
     }
   };
@@ -283,45 +202,26 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
       for (int kt = 0; kt < BN / 32; ++kt) {
         const int k0 = n0 + 32 * kt;
         if (causal && k0 > wr0 + 31) break;  // this half is entirely above the diagonal
-        // S^T tile: keys k0 + [0, 32) x this wave's 32 rows.
-        // d <= 128: all K operands of the piece are read before the MFMAs that use them, and
-        // the V^T operands right after, so LDS latency hides behind the MFMAs and the softmax.
+        // S^T tile: keys k0 + [0, 32) x this wave's 32 rows.  All K operands of the piece
+        // are read before the MFMAs that use them, and the V^T operands right after, so LDS
+        // latency hides behind the MFMAs and the softmax.
         const bf16_t* kp = sK + (32 * kt + l32) * KSTR + 8 * hh;
         const bf16_t* vp = sV + l32 * VSTR + 8 * hh + 32 * kt;
         // V^T operand j = 2 dt + c2 (head-dim tile dt, key half c2)
         auto vread = [&](int j) { return lds_read_b128(vp + 32 * (j >> 1) * VSTR + 16 * (j & 1)); };
         f32x16 s = zero16();
-        bf16x8 vop[kStream ? kRing : 2 * ND];
-        if constexpr (kStream) {
-          // d = 256 (one wave per SIMD, the whole register file): operands stream through a
-          // ring of kRing registers, read kAhead products ahead, so that the Q operands keep
-          // their VGPRs.
-          bf16x8 kop[kRing];
+        bf16x8 vop[2 * ND];
+        bf16x8 kop[NC];
 #pragma unroll
-          for (int i = 0; i < kAhead; ++i) kop[i] = lds_read_b128(kp + 16 * i);
-          __builtin_amdgcn_s_setprio(1);
+        for (int cc = 0; cc < NC; ++cc) kop[cc] = lds_read_b128(kp + 16 * cc);
+        // Raised wave priority over each MFMA run: the other wave on the SIMD gets the
+        // softmax VALU slots while this one keeps the matrix core fed.
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) {
-            if (cc + kAhead < NC) kop[(cc + kAhead) % kRing] = lds_read_b128(kp + 16 * (cc + kAhead));
-            s = mfma32(kop[cc % kRing], qop[cc], s);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-          __builtin_amdgcn_s_setprio(0);
+        for (int cc = 0; cc < NC; ++cc) s = mfma32(kop[cc], qop[cc], s);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-          for (int i = 0; i < kAhead; ++i) vop[i] = vread(i);
-        } else {
-          bf16x8 kop[NC];
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) kop[cc] = lds_read_b128(kp + 16 * cc);
-          // Raised wave priority over each MFMA run: the other wave on the SIMD gets the
-          // softmax VALU slots while this one keeps the matrix core fed.
-          __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) s = mfma32(kop[cc], qop[cc], s);
-          __builtin_amdgcn_s_setprio(0);
-#pragma unroll
-          for (int j = 0; j < 2 * ND; ++j) vop[j] = vread(j);
-        }
+        for (int j = 0; j < 2 * ND; ++j) vop[j] = vread(j);
 
         // Online softmax.  In a piece that crosses the mask band (or the end of the
         // sequence) the masked scores are first replaced by -inf under a wave-uniform branch;
@@ -403,17 +303,8 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
 
         // O^T += V^T P^T.
         __builtin_amdgcn_s_setprio(1);
-        if constexpr (kStream) {
 #pragma unroll
-          for (int j = 0; j < 2 * ND; ++j) {
-            if (j + kAhead < 2 * ND) vop[(j + kAhead) % kRing] = vread(j + kAhead);
-            acc[j >> 1] = mfma32(vop[j % kRing], pp[j & 1], acc[j >> 1]);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 2 * ND; ++j) acc[j >> 1] = mfma32(vop[j], pp[j & 1], acc[j >> 1]);
-        }
+        for (int j = 0; j < 2 * ND; ++j) acc[j >> 1] = mfma32(vop[j], pp[j & 1], acc[j >> 1]);
         __builtin_amdgcn_s_setprio(0);
       }
     }
@@ -423,6 +314,389 @@ __global__ __launch_bounds__(FwdCfg<D>::NT, 1) void fwd_bf16_kernel(
     }
     __syncthreads();
   }
+
+  // Epilogue: O = acc / l (one rounding to bf16), LSE = (m + log2 l) * ln 2.
+  const float l = half_sum(l_i);
+  const float le = half_sum(le_i);
+  if (row < N) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    bf16_t* orow = O + ((size_t)seq0 + row) * qs + (size_t)hq * D;
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const bf16x2 lo = to_bf16x2(acc[dt][4 * g4] * inv, acc[dt][4 * g4 + 1] * inv);
+        const bf16x2 hi = to_bf16x2(acc[dt][4 * g4 + 2] * inv, acc[dt][4 * g4 + 3] * inv);
+        uint2 u;
+        u.x = __builtin_bit_cast(uint32_t, lo);
+        u.y = __builtin_bit_cast(uint32_t, hi);
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * g4 + 4 * hh) = u;
+      }
+    }
+    if (hh == 0)
+      LSE[lse0 + row] = le > 0.f ? (m_i + __log2f(le)) * kLn2 : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// bf16 forward for d = 256: 4 waves x 32 query rows = 128 rows of one (batch entry, query
+// head) per workgroup, 32-key tiles, one wave per SIMD.  With no second wave on a SIMD to
+// take the exponentials while the other wave's products run, each wave overlaps the two
+// itself: during step t it computes the scores of tile t + 1 (S^T = K Q^T, 16 products)
+// and, between those products, the weights of tile t (one score element per product); the
+// O^T products of tile t follow.  K tiles are therefore staged one tile ahead of V tiles
+// (K of tile t + 1 and V of tile t are in LDS during step t, each in its own pair of
+// buffers).  The 128 O^T accumulator registers live in AGPRs (assembly products), which
+// leaves the VGPRs for Q, two score tiles and the staging registers.  Everything else (mask
+// band, lazy reference max, rounded-weight sums, tile order, epilogue) is as in
+// fwd_bf16_kernel.
+struct D256Cfg {
+  static constexpr int D = 256;
+  static constexpr int NT = 256;       // 4 waves
+  static constexpr int BM = 128;       // query rows per workgroup
+  static constexpr int BN = 32;        // keys per tile
+  static constexpr int KSTR = D + 8;   // K tile row stride in elements (16-byte pad)
+  static constexpr int VSTR = BN + 8;  // V^T tile row stride in elements (16-byte pad)
+  static constexpr int K_ELEMS = BN * KSTR;
+  static constexpr int V_ELEMS = D * VSTR;
+  static constexpr int LDS_BYTES = 2 * (K_ELEMS + V_ELEMS) * 2;  // two K and two V^T buffers
+};
+
+template <int AL>
+__global__ __launch_bounds__(D256Cfg::NT, 1) void fwd_bf16_d256_kernel(
+    const bf16_t* __restrict__ Q, const bf16_t* __restrict__ K, const bf16_t* __restrict__ V,
+    bf16_t* __restrict__ O, float* __restrict__ LSE, int B, int Hq, int Hkv, int Nmax,
+    int causal, int window, float c, int neg_q, const int* __restrict__ cu, int ntot,
+    const float* __restrict__ slopes) {
+  using Cfg = D256Cfg;
+  constexpr int D = Cfg::D, NT = Cfg::NT, BM = Cfg::BM, BN = Cfg::BN;
+  constexpr int KSTR = Cfg::KSTR, VSTR = Cfg::VSTR;
+  constexpr int NC = D / 16;  // k-steps of S^T over the head dim
+  constexpr int ND = D / 32;  // 32-wide head-dim tiles of O^T
+  constexpr int kRing = 4, kAhead = 3;  // operand ring: registers, products read ahead
+  static_assert(NC == 16, "one score element of the previous tile per S^T product");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16_t* lds = reinterpret_cast<bf16_t*>(smem);
+  auto kbuf = [&](int i) { return lds + i * Cfg::K_ELEMS; };
+  auto vbuf = [&](int i) { return lds + 2 * Cfg::K_ELEMS + i * Cfg::V_ELEMS; };
+
+  const int num_m = (Nmax + BM - 1) / BM;
+  int b, hq, rank;
+  work_item(B, Hq, num_m, b, hq, rank);
+  const int mb = num_m - 1 - rank;  // causal: the last row block attends the most keys
+  const int hkv = hq / (Hq / Hkv);
+  int seq0, N;  // first row and length of this batch entry's sequence
+  seq_span(cu, ntot, b, Nmax, seq0, N);
+  if (mb * BM >= N) return;  // a row block past the end of a shorter packed sequence
+  const size_t lse0 = stat_base(cu, ntot, b, Hq, hq, Nmax, seq0);
+  const float slope2 = AL != 0 ? slopes[hq] * kLog2e : 0.f;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = wave_id();
+  const int hh = lane >> 5, l32 = lane & 31;
+  const int m0 = mb * BM;
+  const int wr0 = m0 + w * 32;
+  const int row = wr0 + l32;
+
+  const size_t qs = (size_t)Hq * D, ks = (size_t)Hkv * D;
+  const bf16_t* Qh = Q + ((size_t)seq0 * Hq + hq) * D;
+  const bf16_t* Kh = K + ((size_t)seq0 * Hkv + hkv) * D;
+  const bf16_t* Vh = V + ((size_t)seq0 * Hkv + hkv) * D;
+
+  // Q^T operand: lane holds Q[row][16c + 8hh .. +7] for every k-step c.
+  bf16x8 qop[NC];
+  if (row < N) {
+    const bf16_t* qr = Qh + (size_t)row * qs + 8 * hh;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      qop[cc] = __builtin_bit_cast(bf16x8, gload16(qr + 16 * cc));
+      if (neg_q) qop[cc] = negate8(qop[cc]);
+    }
+  } else {
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) qop[cc] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+  }
+
+  // Key range any row of this workgroup may attend.
+  int kv_lo = 0, kv_hi = N;
+  if (causal) kv_hi = min(N, m0 + BM);
+  if (window > 0) kv_lo = max(0, m0 - window + 1);
+  const int nb_lo = kv_lo / BN, nb_hi = (kv_hi + BN - 1) / BN;
+
+  // Staging.  K: the tile's 32 x 32 16-byte chunks, four per thread, stored row-major.
+  // V: one (4-key group, 8-dim chunk) task per thread, transposed in registers; key groups
+  // run fastest, so the 16 lanes the LDS writes per cycle of an 8-byte transposed store span
+  // all eight key groups of the tile and two chunks, two lanes per bank.  Tiles are read
+  // through buffer resources whose size ends at row N, so rows past the end of the
+  // sequence load as zeros.
+  constexpr int CPR = D / 8;      // 16-byte chunks per K/V row
+  constexpr int PTK = BN * CPR / NT;
+  static_assert(BN * CPR == PTK * NT && (BN / 4) * CPR == NT, "whole staging tasks per thread");
+  const uint32_t row_bytes = (uint32_t)ks * 2u;
+  // two register sets: the loads of step t land in set t % 2 and are stored in step t + 2
+  uint4 kr[2][PTK], vr[2][4];
+  uint32_t koff[PTK];
+#pragma unroll
+  for (int i = 0; i < PTK; ++i) {
+    const int ch = tid + NT * i;
+    koff[i] = (uint32_t)((ch / CPR) * ks + (ch % CPR) * 8) * 2u;
+  }
+  const int vkg = tid % (BN / 4), vdc = tid / (BN / 4);
+  const uint32_t voff = (uint32_t)(4 * vkg * ks + vdc * 8) * 2u;
+  // Staging pieces, so that they can sit between matrix products.  A K piece is one of the
+  // thread's four chunks, a V piece two rows of its transposed task.
+  auto tile_rsrc = [&](const bf16_t* base, int nb) {
+    const int n0 = nb * BN;
+    return make_rsrc(base + (size_t)n0 * ks, (uint32_t)(N - n0) * row_bytes);
+  };
+  auto kload = [&](int rs, const rsrc_t& res, int i) { kr[rs][i] = bload16(res, koff[i]); };
+  auto vload = [&](int rs, const rsrc_t& res, int e) {
+    vr[rs][e] = bload16(res, voff + e * row_bytes);
+  };
+  auto kstore = [&](int rs, int buf, int i) {
+    const int ch = tid + NT * i;
+    *reinterpret_cast<uint4*>(kbuf(buf) + (ch / CPR) * KSTR + (ch % CPR) * 8) = kr[rs][i];
+  };
+  auto vstore = [&](int rs, int buf, int m) {
+    bf16_t* dst = vbuf(buf) + (vdc * 8) * VSTR + vt_pos(4 * vkg);
+    const uint32_t a0 = word(vr[rs][0], m), a1 = word(vr[rs][1], m);
+    const uint32_t a2 = word(vr[rs][2], m), a3 = word(vr[rs][3], m);
+    uint2 even, odd;  // dims 2m and 2m+1, keys 0..3 of the group
+    even.x = pack_lo(a0, a1);
+    even.y = pack_lo(a2, a3);
+    odd.x = pack_hi(a0, a1);
+    odd.y = pack_hi(a2, a3);
+    *reinterpret_cast<uint2*>(dst + (2 * m) * VSTR) = even;
+    *reinterpret_cast<uint2*>(dst + (2 * m + 1) * VSTR) = odd;
+  };
+
+  // Running state of this lane's row, as in fwd_bf16_kernel.
+  float m_i = -INFINITY, l_i = 0.f, le_i = 0.f;
+  f32x16 acc[ND];
+#pragma unroll
+  for (int i = 0; i < ND; ++i) acc[i] = zero16();
+  acc_written(acc);
+  bf16x2 ones;
+  ones[0] = (__bf16)1.f;
+  ones[1] = (__bf16)1.f;
+  const int klo = window > 0 ? row - window + 1 : 0;  // allowed keys of this row: [klo, khi]
+  const int khi = causal ? min(row, N - 1) : N - 1;
+
+  // Tile order, as in fwd_bf16_kernel.
+  const int ntiles = nb_hi - nb_lo;
+  const int nd = min(max((m0 + BM / 2) / BN, nb_lo), max(nb_hi - 1, nb_lo));
+  const int zl = nd - nb_lo, zu = nb_hi - 1 - nd, zm = min(zl, zu);
+  auto tile = [&](int t) {
+    if constexpr (AL == 0) {
+      return nb_lo + t;
+    } else if constexpr (AL == 1) {
+      return nb_hi - 1 - t;
+    } else {
+      if (t <= 2 * zm) return nd + ((t & 1) ? (t + 1) / 2 : -(t / 2));
+      return zu > zl ? nd + (t - zm) : nd - (t - zm);
+    }
+  };
+  // whether this wave has an allowed (row, key) pair in tile t (wave-uniform)
+  auto active = [&](int t) {
+    const int n0 = tile(t) * BN;
+    return wr0 < N && (!causal || n0 <= wr0 + 31) &&
+           (window <= 0 || n0 + BN - 1 >= wr0 - window + 1);
+  };
+
+  const bf16_t* kp0 = lds + l32 * KSTR + 8 * hh;  // this lane's K row, buffer 0
+  // S^T of the tile in K buffer kb, without anything beside the products.
+  auto scores = [&](int kb, f32x16& s) {
+    const bf16_t* kp = kp0 + kb * Cfg::K_ELEMS;
+    bf16x8 kop[kRing];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) kop[i] = lds_read_b128(kp + 16 * i);
+    s = zero16();
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      if (cc + kAhead < NC) kop[(cc + kAhead) % kRing] = lds_read_b128(kp + 16 * (cc + kAhead));
+      s = mfma32(kop[cc % kRing], qop[cc], s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto koffs = [](int r) { return (float)(8 * (r >> 2) + (r & 3)); };
+  // Step t: weights and O^T products of tile t (scores in sc), scores of tile t + 1 into sn.
+  // Staging in step t, from and into register set rs = t % 2: K of tile t + 2 replaces K of
+  // tile t (read during step t - 1), V of tile t + 1 replaces V of tile t - 1, then the
+  // loads of K of tile t + 4 and V of tile t + 3 for step t + 2.  Past the last tile the
+  // indices are clamped: a store then fills a buffer no later step reads, and a load reads
+  // the last tile again.
+  auto step = [&](int t, int rs, f32x16& sc, f32x16& sn) {
+    const int tl = ntiles - 1;
+    const bool more = t + 1 < ntiles;
+    const bool act = active(t), act_n = more && active(t + 1);
+    const rsrc_t kres = tile_rsrc(Kh, tile(min(t + 4, tl)));
+    const rsrc_t vres = tile_rsrc(Vh, tile(min(t + 3, tl)));
+    // staging piece j of 16: K stores, V stores, K loads, V loads
+    auto stage = [&](int j) {
+      if (j < 4) kstore(rs, t & 1, j);
+      else if (j < 8) vstore(rs, (t + 1) & 1, j - 4);
+      else if (j < 12) kload(rs, kres, j - 8);
+      else vload(rs, vres, j - 12);
+    };
+    if (act) {
+      const int k0 = tile(t) * BN;
+      // (bitwise, not short-circuit: a branch-free scalar condition)
+      const bool need_mask = (k0 + 32 > N) | ((causal != 0) & (k0 + 31 > wr0)) |
+                             ((window > 0) & (k0 < wr0 + 32 - window));
+      if (need_mask) {
+        const int kb0 = k0 + hh * 4;  // key of element r: kb0 + (r / 4) * 8 + r % 4
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb0 + (r >> 2) * 8 + (r & 3);
+          sc[r] = ((key >= klo) & (key <= khi)) ? sc[r] : -INFINITY;
+        }
+      }
+      const float dbase = AL != 0 ? (float)(k0 + 4 * hh - row) : 0.f;
+      float e[16], q[8];
+      if (act_n) {
+        // Products of tile t + 1 with the weights of tile t between them: product cc, then
+        // weight cc and the pair sum of the weights two before.  (The empty assembly keeps
+        // the compiler from hoisting the exponent arguments out of this loop.)
+        float mref = m_i;
+        asm volatile("" : "+v"(mref));
+        const bf16_t* kp = kp0 + ((t + 1) & 1) * Cfg::K_ELEMS;
+        bf16x8 kop[kRing];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) kop[i] = lds_read_b128(kp + 16 * i);
+        sn = zero16();
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          if (cc + kAhead < NC) kop[(cc + kAhead) % kRing] = lds_read_b128(kp + 16 * (cc + kAhead));
+          sn = mfma32(kop[cc % kRing], qop[cc], sn);
+          e[cc] = fast_exp2(fmaf(sc[cc], c, alibi_addend<AL>(slope2, dbase, koffs(cc), mref)));
+          if (cc >= 2 && (cc & 1) == 0) q[cc / 2 - 1] = e[cc - 2] + e[cc - 1];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        q[7] = e[14] + e[15];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          e[r] = fast_exp2(fmaf(sc[r], c, alibi_addend<AL>(slope2, dbase, koffs(r), m_i)));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = e[2 * i] + e[2 * i + 1];
+      }
+      float rse = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+
+      // V^T operands of tile t: j = 8 half + dt (head-dim tile dt, key half), so the
+      // products of the first key half can run while the second half's weights convert.
+      const bf16_t* vp = vbuf(t & 1) + l32 * VSTR + 8 * hh;
+      auto vread = [&](int j) { return lds_read_b128(vp + 32 * (j & 7) * VSTR + 16 * (j >> 3)); };
+      bf16x8 vop[kRing];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) vop[i] = vread(i);
+
+      if (__any(!(rse <= kSumLimit))) {  // wave-uniform; rare after a row's first tile
+        float mt;
+        if constexpr (AL == 0) {
+          float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+          for (int r = 2; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sc[r]), sc[r + 1]);  // v_max3
+          mx = half_max(mx);
+          mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+        } else {  // the maximum of the biased scores
+          float mx = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            mx = fmaxf(mx, fmaf(sc[r], c, alibi_addend<AL>(slope2, dbase, koffs(r), 0.f)));
+          mt = half_max(mx);
+        }
+        const bool grow = mt > m_i + kRescaleThreshold;
+        const float alpha = grow ? fast_exp2(m_i - mt) : 1.f;  // 0 when m_i was -inf
+        l_i *= alpha;
+        le_i *= alpha;
+        acc_ready(acc);
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+        acc_written(acc);
+        m_i = grow ? mt : m_i;
+        const float m_use = (m_i == -INFINITY) ? 0.f : m_i;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          e[r] = fast_exp2(fmaf(sc[r], c, alibi_addend<AL>(slope2, dbase, koffs(r), m_use)));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = e[2 * i] + e[2 * i + 1];
+        rse = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+      }
+      // Rounded weights of key half h: P^T operand pp[h], its sum into its own dot chain.
+      bf16x8 pp[2];
+      float rs2[2] = {l_i, 0.f};
+      auto convert = [&](int h) {
+#pragma unroll
+        for (int r = 8 * h; r < 8 * h + 8; r += 2) {
+          const bf16x2 pe = to_bf16x2(e[r], e[r + 1]);
+          rs2[h] = __builtin_amdgcn_fdot2_f32_bf16(pe, ones, rs2[h], false);
+          pp[h][r & 7] = pe[0];
+          pp[h][(r & 7) + 1] = pe[1];
+        }
+        operand_ready(pp[h]);
+      };
+      convert(0);
+
+      // O^T += V^T P^T, with the staging pieces and the second half's weights between the
+      // products.
+#pragma unroll
+      for (int j = 0; j < 2 * ND; ++j) {
+        if (j + kAhead < 2 * ND) vop[(j + kAhead) % kRing] = vread(j + kAhead);
+        if (j == ND) convert(1);
+        mfma_acc(acc[j & 7], vop[j % kRing], pp[j >> 3]);
+        stage(j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_i = rs2[0] + rs2[1];
+      le_i += rse;
+    } else {
+      if (act_n) scores((t + 1) & 1, sn);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) stage(j);
+    }
+    __syncthreads();
+  };
+
+  f32x16 sa = zero16(), sb = zero16();
+  if (ntiles > 0) {
+    const int tl = ntiles - 1;
+    // LDS: K of tiles 0 and 1, V of tile 0.  Register set 0: K of tile 2, V of tile 1; set
+    // 1: K of tile 3, V of tile 2.
+#pragma unroll
+    for (int i = 0; i < PTK; ++i) kload(0, tile_rsrc(Kh, tile(0)), i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vload(0, tile_rsrc(Vh, tile(0)), e);
+#pragma unroll
+    for (int i = 0; i < PTK; ++i) kload(1, tile_rsrc(Kh, tile(min(1, tl))), i);
+#pragma unroll
+    for (int i = 0; i < PTK; ++i) kstore(0, 0, i);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) vstore(0, 0, m);
+#pragma unroll
+    for (int i = 0; i < PTK; ++i) kstore(1, 1, i);
+#pragma unroll
+    for (int i = 0; i < PTK; ++i) kload(0, tile_rsrc(Kh, tile(min(2, tl))), i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vload(0, tile_rsrc(Vh, tile(min(1, tl))), e);
+#pragma unroll
+    for (int i = 0; i < PTK; ++i) kload(1, tile_rsrc(Kh, tile(min(3, tl))), i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vload(1, tile_rsrc(Vh, tile(min(2, tl))), e);
+    __syncthreads();
+    if (active(0)) scores(0, sa);
+    __syncthreads();  // K buffer 0 is rewritten during step 0
+  }
+  // Whole pairs of steps in the loop, so that every path into a step has issued the other
+  // register set's loads after this set's and the load waits can leave them in flight.
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, 0, sa, sb);
+    step(t + 1, 1, sb, sa);
+  }
+  if (t < ntiles) step(t, 0, sa, sb);
+  acc_ready(acc);
 
   // Epilogue: O = acc / l (one rounding to bf16), LSE = (m + log2 l) * ln 2.
   const float l = half_sum(l_i);
@@ -562,15 +836,35 @@ static hipError_t launch_fwd_bf16_d(const FwdArgs& a, hipStream_t st) {
 
 template <int D>
 static hipError_t launch_fwd_bf16_al(const FwdArgs& a, hipStream_t st) {
+  static_assert(D <= 128, "head dim 256: launch_fwd_bf16_d256");
   if (a.slopes == nullptr) return launch_fwd_bf16_d<D, 0>(a, st);
   return a.causal ? launch_fwd_bf16_d<D, 1>(a, st) : launch_fwd_bf16_d<D, 2>(a, st);
+}
+
+template <int AL>
+static hipError_t launch_fwd_bf16_d256(const FwdArgs& a, hipStream_t st) {
+  using Cfg = D256Cfg;
+  // Dynamic LDS limit, set once (a function-local static: the first call is thread-safe).
+  static const hipError_t attr = hipFuncSetAttribute((const void*)fwd_bf16_d256_kernel<AL>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     Cfg::LDS_BYTES);
+  if (attr != hipSuccess) return attr;
+  const int num_m = (a.N + Cfg::BM - 1) / Cfg::BM;
+  const int grid = a.B * a.Hq * num_m;
+  hipLaunchKernelGGL((fwd_bf16_d256_kernel<AL>), dim3(grid), dim3(Cfg::NT), Cfg::LDS_BYTES, st,
+                     (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (bf16_t*)a.o,
+                     a.lse, a.B, a.Hq, a.Hkv, a.N, a.causal, a.window, a.c_log2, a.neg_q, a.cu,
+                     a.ntot, a.slopes);
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t st) {
   switch (a.d) {
     case 64: return launch_fwd_bf16_al<64>(a, st);
     case 128: return launch_fwd_bf16_al<128>(a, st);
-    case 256: return launch_fwd_bf16_al<256>(a, st);
+    case 256:
+      if (a.slopes == nullptr) return launch_fwd_bf16_d256<0>(a, st);
+      return a.causal ? launch_fwd_bf16_d256<1>(a, st) : launch_fwd_bf16_d256<2>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,7 +1,8 @@
 """Build checks on the CPU (hipcc cross-compiles for gfx950 without a GPU).
 
-The last check reads the generated assembly of the head-dim-256 key-block kernel, whose
-dK/dV products are inline assembly with hand-written wait states (see there).
+The last two checks read the generated assembly of the head-dim-256 key-block kernel and
+the head-dim-256 forward, whose dK/dV and O products are inline assembly with hand-written
+wait states (see there).
 
 No kernel may use scratch memory (register spills to memory inside an inner loop cost more
 than the changes that would cause one save).  The kernels for head dims 64 and 128 must
@@ -61,8 +62,8 @@ def usage():
 
 def test_every_attention_kernel_is_reported(usage):
     names = " ".join(usage)
-    for k in ("fwd_bf16_kernel", "fwd_fp8_kernel", "bwd_dkdv8_kernel", "bwd_dq_kernel",
-              "bwd_pre_kernel", "decode_kernel"):
+    for k in ("fwd_bf16_kernel", "fwd_bf16_d256_kernel", "fwd_fp8_kernel", "bwd_dkdv8_kernel",
+              "bwd_dq_kernel", "bwd_pre_kernel", "decode_kernel"):
         assert k in names, k
 
 
@@ -83,8 +84,10 @@ def test_no_kernel_uses_scratch_memory(usage):
 
 def test_head_dim_256_kernels_are_covered(usage):
     names = " ".join(n for n in usage if "ILi256E" in n)
-    for k in ("fwd_bf16_kernel", "fwd_fp8_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
+    for k in ("fwd_fp8_kernel", "bwd_dkdv_kernel", "bwd_dq_kernel"):
         assert k in names, k
+    # the bf16 forward has a kernel of its own for d = 256 (templated on the bias only)
+    assert sum("fwd_bf16_d256_kernel" in n for n in usage) == 3
 
 
 # The head-dim-256 key-block kernel accumulates dK and dV in AGPRs through matrix products
@@ -161,3 +164,52 @@ def test_head_dim_256_key_block_kernel_fences_its_agpr_products(bwd_asm):
         assert reads and min(reads) > max(ready), name
         writes = [i for i in acc_moves if not body[i].startswith("v_accvgpr_read")]
         assert writes and max(writes) < min(written), name
+
+
+@pytest.fixture(scope="module")
+def fwd_asm():
+    if shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"):
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as tmpdir:
+        out = os.path.join(tmpdir, "fa_fwd.s")
+        cmd = ([B.hipcc()] + B.HIPCC_FLAGS + B.FILE_FLAGS.get("fa_fwd.hip", []) +
+               ["--cuda-device-only", "-S", os.path.join(B.CSRC, "fa_fwd.hip"), "-o", out])
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-2000:]
+        with open(out) as f:
+            return f.read()
+
+
+# The head-dim-256 forward keeps O in AGPRs through assembly products too, and touches the
+# accumulators with vector instructions in three places: zeroing (before the first
+# product), the rare rescale of the running sums (between products) and the epilogue.  In
+# the order the code is laid out, every such read must follow a long fence that comes after
+# the last product, and every write must be followed by the short fence before the next
+# product.
+def test_head_dim_256_forward_fences_its_agpr_products(fwd_asm):
+    bodies = _function_bodies(fwd_asm, "_ZN2fa20fwd_bf16_d256_kernel")
+    assert len(bodies) == 3, list(bodies)  # unbiased, causal and general position bias
+    for name, body in bodies.items():
+        blocks = dict(_asm_blocks(body))
+        n_products = 0
+        last_product = ready_after = -1
+        pending_write = False
+        for i, line in enumerate(body):
+            text = blocks.get(i)
+            if text is not None and "v_mfma" in text:
+                m = ASM_PRODUCT.search(text)
+                assert m and m.group(1, 2) == m.group(3, 4), (name, text)
+                assert not pending_write, (name, i, "product after an unfenced AGPR write")
+                n_products += 1
+                last_product = i
+            elif text is not None and text.split() == ["s_nop", "7", "s_nop", "7", "s_nop", "7"]:
+                ready_after = i
+            elif text is not None and text.strip() == "s_nop 4":
+                pending_write = False
+            elif line.startswith("v_accvgpr_read"):
+                assert ready_after > last_product, (name, i, "AGPR read without the long fence")
+            elif line.startswith("v_accvgpr_write") or line.startswith("v_accvgpr_mov"):
+                pending_write = True
+        # 16 O^T products per step; the loop body holds two steps, the odd last step a third
+        assert n_products == 48, (name, n_products)
+        assert not pending_write, name
