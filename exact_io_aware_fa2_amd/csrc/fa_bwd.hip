@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int NDH = D / 32;  // 32-wide head-dim tiles of dK^T / dV^T
   constexpr int BUFB = Cfg::BUF * 2 + 2 * BQ * 4;  // bytes per buffer
   constexpr int kRing = 4, kAh = 3;  // operand rings (see the step loop)
-  // dK^T / dV^T in AGPRs through the assembly products (all 256 of them at d = 256)
-  constexpr bool kAcc = NDH == 8;
+  // dK^T / dV^T in AGPRs through the assembly products (all 256 of them)
+  static_assert(D == 256 && MT == 1, "the key-block kernel for d = 256 (d <= 128: bwd_dkdv8_kernel)");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int num_kb = (Nmax + BKN - 1) / BKN;
@@ -215,10 +215,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     dk[i] = zero16();
     dv[i] = zero16();
   }
-  if constexpr (kAcc) {
-    acc_written(dk);
-    acc_written(dv);
-  }
+  acc_written(dk);
+  acc_written(dv);
 
   // Staging: a task = 4 rows x 8 dims of Q and of dO, stored row-major and transposed.
   constexpr int CPR = D / 8;
@@ -299,129 +297,98 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     const bool active = kw0 < N && (!causal || r0 + BQ - 1 >= kw0) &&
                         (window <= 0 || r0 <= kw0 + 31 + window - 1);
     if (active) {
-      // S = Q K^T and dP = dO V^T for this wave's 32 keys (lane = key, rows in registers).
-      f32x16 s[MT], dp[MT];
+      // One step = four product phases of 16 products each, every product with one A
+      // operand from LDS read kAh products ahead through one ring: S = Q K^T, dP = dO V^T
+      // (lane = key, rows in registers), dV^T += dO^T P, dK^T += Q^T dS.  The vector work
+      // sits between the products of the phase after the one it depends on: the weights
+      // P = exp2(S c + bias - LSE log2 e) between the dP products (one per product), dS =
+      // P (dP - D) between the dV products.  With one wave per SIMD nothing else would run
+      // beside the products.
+      f32x16 s = zero16(), dp;
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16_t* qa = sQ + (32 * mt + l32) * STR + 8 * hh;
-        const bf16_t* oa = sO + (32 * mt + l32) * STR + 8 * hh;
-        s[mt] = zero16();
+      for (int g4 = 0; g4 < 4; ++g4) {  // dP - D straight out of the products
+        const f32x4 nd4 = *reinterpret_cast<const f32x4*>(sD + 8 * g4 + 4 * hh);
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {  // dP - D straight out of the products
-          const f32x4 nd4 = *reinterpret_cast<const f32x4*>(sD + 32 * mt + 8 * g4 + 4 * hh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dp[mt][4 * g4 + e] = nd4[e];
-        }
-        // The Q / dO operands stream through rings of kRing registers read kAh k-steps
-        // ahead (a scheduling barrier per k-step keeps the reads from being hoisted or sunk):
-        // with K and V resident the register file has no room for all of them at once, and
-        // reads placed right before their products leave the LDS latency exposed with one
-        // wave per SIMD.
-        bf16x8 qa_op[kRing], oa_op[kRing];
-#pragma unroll
-        for (int i = 0; i < kAh; ++i) {
-          qa_op[i] = lds_read_b128(qa + 16 * i);
-          oa_op[i] = lds_read_b128(oa + 16 * i);
-        }
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          if (cc + kAh < NC) {
-            qa_op[(cc + kAh) % kRing] = lds_read_b128(qa + 16 * (cc + kAh));
-            oa_op[(cc + kAh) % kRing] = lds_read_b128(oa + 16 * (cc + kAh));
-          }
-          s[mt] = mfma32(qa_op[cc % kRing], kop[cc], s[mt]);
-          dp[mt] = mfma32(oa_op[cc % kRing], vop[cc], dp[mt]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int e = 0; e < 4; ++e) dp[4 * g4 + e] = nd4[e];
       }
-      // A operands of the dV / dK products through rings: product j = (head-dim tile
-      // j / (2 MT), k-step j % (2 MT)).  The first slot is read here, so its latency hides
-      // behind the softmax (more slots this early spill at d = 256).
-      constexpr int NJ = NDH * 2 * MT;
-      auto aread = [&](const bf16_t* base, int j) {
-        return lds_read_b128(base + (32 * (j / (2 * MT)) + l32) * TSTR + 8 * hh + 16 * (j % (2 * MT)));
-      };
-      bf16x8 ao[kRing], aq[kRing];
-      ao[0] = aread(sOT, 0);
-      aq[0] = aread(sQT, 0);
-      // P = exp2(S c + bias - LSE log2 e), masked entries 0 (selects under a wave-uniform
-      // branch).  The position bias: see alibi_addend (here the lane is the key).
+      const bf16_t* qa = sQ + l32 * STR + 8 * hh;
+      const bf16_t* oa = sO + l32 * STR + 8 * hh;
+      auto rowread = [&](int p) { return lds_read_b128((p < NC ? qa : oa) + 16 * (p % NC)); };
+      bf16x8 ring[kRing];
+#pragma unroll
+      for (int i = 0; i < kAh; ++i) ring[i] = rowread(i);
+#pragma unroll
+      for (int p = 0; p < NC; ++p) {
+        ring[(p + kAh) % kRing] = rowread(p + kAh);
+        s = mfma32(ring[p % kRing], kop[p], s);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // The position bias: see alibi_addend (here the lane is the key).
       const float sl2 = slope_of(it);
       const float kstep = sl2 * (float)(key - r0);
       const float rbase = (float)(r0 + 4 * hh - key);
+      auto lse4 = [&](int g4) { return *reinterpret_cast<const f32x4*>(sL + 8 * g4 + 4 * hh); };
+      f32x4 L4 = lse4(0);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 L4 = *reinterpret_cast<const f32x4*>(sL + 32 * mt + 8 * g4 + 4 * hh);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float xr = AL == 1 ? kstep - L4[e]
-                                     : alibi_addend<AL>(sl2, rbase, (float)(32 * mt + 8 * g4 + e),
-                                                        L4[e]);
-            s[mt][4 * g4 + e] = fast_exp2(fmaf(s[mt][4 * g4 + e], c, xr));
-          }
-        }
+      for (int cc = 0; cc < NC; ++cc) {
+        const int p = NC + cc;
+        if (p + kAh < 2 * NC) ring[(p + kAh) % kRing] = rowread(p + kAh);
+        dp = mfma32(ring[p % kRing], vop[cc], dp);
+        const int g4 = cc >> 2, e = cc & 3;
+        if (e == 0 && g4 > 0) L4 = lse4(g4);
+        const float xr = AL == 1 ? kstep - L4[e]
+                                 : alibi_addend<AL>(sl2, rbase, (float)(8 * g4 + e), L4[e]);
+        s[cc] = fast_exp2(fmaf(s[cc], c, xr));
+        __builtin_amdgcn_sched_barrier(0);
       }
+      // A operands of the dV / dK products: product j = 8 k + dt (key-row half k, head-dim
+      // tile dt) of dV, then the same of dK; the 8 rows of a k-step are contiguous in the
+      // transposed tiles.
+      auto aread = [&](int j) {
+        const bf16_t* base = j < 2 * NDH ? sOT : sQT;
+        const int jj = j % (2 * NDH);
+        return lds_read_b128(base + (32 * (jj % NDH) + l32) * TSTR + 8 * hh + 16 * (jj / NDH));
+      };
+#pragma unroll
+      for (int i = 0; i < kAh; ++i) ring[i] = aread(i);
       const bool need_mask = (kw0 + 32 > N) | ((causal != 0) & (kw0 + 31 > r0)) |
                              ((window > 0) & (kw0 < r0 + BQ - window));
-      if (need_mask) {
+      if (need_mask) {  // masked weights 0 (selects under a wave-uniform branch)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = r0 + 32 * mt + (r >> 2) * 8 + hh * 4 + (r & 3);
-            const bool ok = (key < N) & (!causal | (key <= row)) &
-                            ((window <= 0) | (key >= row - window + 1));
-            s[mt][r] = ok ? s[mt][r] : 0.f;
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int row = r0 + (r >> 2) * 8 + hh * 4 + (r & 3);
+          const bool ok = (key < N) & (!causal | (key <= row)) &
+                          ((window <= 0) | (key >= row - window + 1));
+          s[r] = ok ? s[r] : 0.f;
         }
       }
-      // dS = P (dP - D); pack P and dS as bf16 B operands (k = query row).
-      bf16x8 pP[MT][2], pS[MT][2];
+      // P and dS as bf16 B operands (k = query row): pP[k] / pS[k] hold elements 8k .. 8k + 7.
+      bf16x8 pP[2], pS[2];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          float dsv[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) dsv[e] = s[mt][4 * g4 + e] * dp[mt][4 * g4 + e];
-          const int c2 = g4 >> 1, i0 = 4 * (g4 & 1);
-          const bf16x2 p01 = to_bf16x2(s[mt][4 * g4], s[mt][4 * g4 + 1]);
-          const bf16x2 p23 = to_bf16x2(s[mt][4 * g4 + 2], s[mt][4 * g4 + 3]);
-          const bf16x2 d01 = to_bf16x2(dsv[0], dsv[1]), d23 = to_bf16x2(dsv[2], dsv[3]);
-          pP[mt][c2][i0] = p01[0];
-          pP[mt][c2][i0 + 1] = p01[1];
-          pP[mt][c2][i0 + 2] = p23[0];
-          pP[mt][c2][i0 + 3] = p23[1];
-          pS[mt][c2][i0] = d01[0];
-          pS[mt][c2][i0 + 1] = d01[1];
-          pS[mt][c2][i0 + 2] = d23[0];
-          pS[mt][c2][i0 + 3] = d23[1];
-        }
+      for (int r = 0; r < 16; r += 2) {
+        const bf16x2 p01 = to_bf16x2(s[r], s[r + 1]);
+        pP[r >> 3][r & 7] = p01[0];
+        pP[r >> 3][(r & 7) + 1] = p01[1];
       }
-      // dV^T += dO^T P and dK^T += Q^T dS (A operands from the transposed tiles: the 8 rows
-      // of a k-step are contiguous).
-      if constexpr (kAcc) operands_ready(pP[0], pS[0]);
+      operand_ready(pP[0]);
+      operand_ready(pP[1]);
 #pragma unroll
-      for (int i = 1; i < kAh; ++i) {
-        ao[i] = aread(sOT, i);
-        aq[i] = aread(sQT, i);
+      for (int j = 0; j < 2 * NDH; ++j) {
+        if (j + kAh < 4 * NDH) ring[(j + kAh) % kRing] = aread(j + kAh);
+        mfma_acc(dv[j % NDH], ring[j % kRing], pP[j / NDH]);
+        if (j % 2 == 1) {  // dS of elements j - 1, j
+          const bf16x2 d01 = to_bf16x2(s[j - 1] * dp[j - 1], s[j] * dp[j]);
+          pS[j >> 3][(j - 1) & 7] = d01[0];
+          pS[j >> 3][j & 7] = d01[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      operand_ready(pS[0]);
+      operand_ready(pS[1]);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        if (j + kAh < NJ) {
-          ao[(j + kAh) % kRing] = aread(sOT, j + kAh);
-          aq[(j + kAh) % kRing] = aread(sQT, j + kAh);
-        }
-        const int dt = j / (2 * MT), kstep = j % (2 * MT);
-        if constexpr (kAcc) {
-          mfma_acc(dv[dt], ao[j % kRing], pP[kstep >> 1][kstep & 1]);
-          mfma_acc(dk[dt], aq[j % kRing], pS[kstep >> 1][kstep & 1]);
-        } else {
-          dv[dt] = mfma32(ao[j % kRing], pP[kstep >> 1][kstep & 1], dv[dt]);
-          dk[dt] = mfma32(aq[j % kRing], pS[kstep >> 1][kstep & 1], dk[dt]);
-        }
+      for (int j = 2 * NDH; j < 4 * NDH; ++j) {
+        if (j + kAh < 4 * NDH) ring[(j + kAh) % kRing] = aread(j + kAh);
+        mfma_acc(dk[j % NDH], ring[j % kRing], pS[(j - 2 * NDH) / NDH]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -432,10 +399,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     __syncthreads();
   }
 
-  if constexpr (kAcc) {
-    acc_ready(dk);
-    acc_ready(dv);
-  }
+  acc_ready(dk);
+  acc_ready(dv);
   if (key < N) {
     bf16_t* dkr = dK + ((size_t)seq0 + key) * ks + (size_t)hkv * D;
     bf16_t* dvr = dV + ((size_t)seq0 + key) * ks + (size_t)hkv * D;
