@@ -222,54 +222,44 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   constexpr int CPR = D / 8;
   constexpr int TASKS = (BQ / 4) * CPR;
   static_assert(BQ % 16 == 0 && CPR % 4 == 0, "task_rc4 needs whole groups of 16 rows and 4 chunks");
-  constexpr int PT = (TASKS + 255) / 256;
-  uint4 qr[PT][4], orr[PT][4];
+  static_assert(TASKS == 256, "one staging task per thread");
+  int srg, sdc;
+  task_rc4<CPR>(tid, srg, sdc);
+  const uint32_t soff = (uint32_t)(4 * srg * qs + 8 * sdc) * 2u;
+  uint4 qr[4], orr[4];
   float lreg = 0.f, dreg = 0.f;
-  auto gload = [&](int it) {
+  // The staging of a step in pieces that can sit between matrix products.  Loads of step
+  // it: part 0 the thread's Q rows, 1 its dO rows, 2 LSE and D.
+  auto gload_part = [&](int it, int part) {
     const int qi = it / G, g = it - qi * G, qb = qblock(qi);
     const int hq = hkv * G + g, r0 = qb * BQ;
-    const bf16_t* Qb = Q + ((size_t)seq0 * Hq + hq) * D;
-    const bf16_t* Ob = dO + ((size_t)seq0 * Hq + hq) * D;
-    const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
-    const rsrc_t qres = make_rsrc(Qb + (size_t)r0 * qs, bytes);
-    const rsrc_t ores = make_rsrc(Ob + (size_t)r0 * qs, bytes);
-#pragma unroll
-    for (int p = 0; p < PT; ++p) {
-      const int task = tid + 256 * p;
-      if (TASKS % 256 == 0 || task < TASKS) {
-        int rg, dc;
-        task_rc4<CPR>(task, rg, dc);
-        const uint32_t off = (uint32_t)(4 * rg * qs + 8 * dc) * 2u;
-        bload_4x8(qr[p], qres, off, (uint32_t)qs * 2u);
-        bload_4x8(orr[p], ores, off, (uint32_t)qs * 2u);
-      }
-    }
-    if (tid < BQ) {
+    if (part < 2) {
+      const bf16_t* base = (part == 0 ? Q : dO) + ((size_t)seq0 * Hq + hq) * D;
+      const uint32_t bytes = (uint32_t)(N - r0) * (uint32_t)qs * 2u;  // rows past N read 0
+      const rsrc_t res = make_rsrc(base + (size_t)r0 * qs, bytes);
+      if (part == 0) bload_4x8(qr, res, soff, (uint32_t)qs * 2u);
+      else bload_4x8(orr, res, soff, (uint32_t)qs * 2u);
+    } else if (tid < BQ) {
       const int n = r0 + tid;
       const size_t li = stat_base(cu, ntot, b, Hq, hq, Nmax, seq0) + n;
       lreg = n < N ? LSE[li] * kLog2e : INFINITY;  // +inf -> P = 0 on padding rows
       dreg = n < N ? Dv[li] : 0.f;
     }
   };
-  auto swrite = [&](int buf, int buf_it) {
+  // Stores into buffer buf for step buf_it: part 0 / 1 the Q / dO rows, 2-5 / 6-9 a quarter
+  // of the transposed Q / dO rows each, 10 LSE and -D.
+  constexpr int kStoreParts = 11, kLoadParts = 3;
+  auto swrite_part = [&](int buf, int buf_it, int part) {
     bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + buf * BUFB);
     bf16_t* sO = sQ + Cfg::SQ;
     bf16_t* sQT = sO + Cfg::SQ;
     bf16_t* sOT = sQT + Cfg::SQT;
     float* sL = reinterpret_cast<float*>(sOT + Cfg::SQT);
-#pragma unroll
-    for (int p = 0; p < PT; ++p) {
-      const int task = tid + 256 * p;
-      if (TASKS % 256 == 0 || task < TASKS) {
-        int rg, dc;
-        task_rc4<CPR>(task, rg, dc);
-        store_4x8_rows(sQ, STR, 4 * rg, 8 * dc, qr[p]);
-        store_4x8_rows(sO, STR, 4 * rg, 8 * dc, orr[p]);
-        store_4x8_transposed(sQT, TSTR, 4 * rg, 8 * dc, qr[p]);
-        store_4x8_transposed(sOT, TSTR, 4 * rg, 8 * dc, orr[p]);
-      }
-    }
-    if (tid < BQ) {
+    if (part == 0) store_4x8_rows(sQ, STR, 4 * srg, 8 * sdc, qr);
+    else if (part == 1) store_4x8_rows(sO, STR, 4 * srg, 8 * sdc, orr);
+    else if (part < 6) store_4x8_transposed_part(sQT, TSTR, 4 * srg, 8 * sdc, qr, part - 2);
+    else if (part < 10) store_4x8_transposed_part(sOT, TSTR, 4 * srg, 8 * sdc, orr, part - 6);
+    else if (tid < BQ) {
       // causal position bias: LSE + slope2 (row - r0) is staged, slope2 (key - r0) added per
       // lane (both small near the diagonal, where the weights are not negligible)
       sL[tid] = AL == 1 ? lreg + slope_of(buf_it) * tid : lreg;
@@ -278,9 +268,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
   };
 
   if (total_it > 0) {
-    gload(0);
-    swrite(0, 0);
-    if (total_it > 1) gload(1);
+#pragma unroll
+    for (int part = 0; part < kLoadParts; ++part) gload_part(0, part);
+#pragma unroll
+    for (int part = 0; part < kStoreParts; ++part) swrite_part(0, 0, part);
+#pragma unroll
+    for (int part = 0; part < kLoadParts; ++part) gload_part(min(1, total_it - 1), part);
   }
   __syncthreads();
   for (int it = 0; it < total_it; ++it) {
@@ -296,6 +289,10 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
     (void)g;
     const bool active = kw0 < N && (!causal || r0 + BQ - 1 >= kw0) &&
                         (window <= 0 || r0 <= kw0 + 31 + window - 1);
+    // Staging in step it: the stores of step it + 1 into the other buffer (read during step
+    // it - 1), then the loads of step it + 2.  Past the last step the stores fill a buffer
+    // no later step reads and the loads repeat the last step's.
+    const int itl = min(it + 2, total_it - 1);
     if (active) {
       // One step = four product phases of 16 products each, every product with one A
       // operand from LDS read kAh products ahead through one ring: S = Q K^T, dP = dO V^T
@@ -376,6 +373,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int j = 0; j < 2 * NDH; ++j) {
         if (j + kAh < 4 * NDH) ring[(j + kAh) % kRing] = aread(j + kAh);
         mfma_acc(dv[j % NDH], ring[j % kRing], pP[j / NDH]);
+        if (j < kStoreParts) swrite_part(buf ^ 1, it + 1, j);
         if (j % 2 == 1) {  // dS of elements j - 1, j
           const bf16x2 d01 = to_bf16x2(s[j - 1] * dp[j - 1], s[j] * dp[j]);
           pS[j >> 3][(j - 1) & 7] = d01[0];
@@ -389,12 +387,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(
       for (int j = 2 * NDH; j < 4 * NDH; ++j) {
         if (j + kAh < 4 * NDH) ring[(j + kAh) % kRing] = aread(j + kAh);
         mfma_acc(dk[j % NDH], ring[j % kRing], pS[(j - 2 * NDH) / NDH]);
+        if (j - 2 * NDH < 2 * kLoadParts && j % 2 == 0) gload_part(itl, (j - 2 * NDH) / 2);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (it + 1 < total_it) {
-      swrite(buf ^ 1, it + 1);
-      if (it + 2 < total_it) gload(it + 2);
+    if (!active) {
+#pragma unroll
+      for (int part = 0; part < kStoreParts; ++part) swrite_part(buf ^ 1, it + 1, part);
+#pragma unroll
+      for (int part = 0; part < kLoadParts; ++part) gload_part(itl, part);
     }
     __syncthreads();
   }

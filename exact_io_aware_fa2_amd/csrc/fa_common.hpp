@@ -233,22 +233,25 @@ __device__ __forceinline__ void store_4x8_rows(bf16_t* lds, int s, int lr0, int 
 }
 
 // Transposed store: LDS row c0 + j (j = 0..7) gets the 4 values of column j at positions
-// tpos(lr0) .. tpos(lr0) + 3 (lr0 a multiple of 4), row stride ts elements.
+// tpos(lr0) .. tpos(lr0) + 3 (lr0 a multiple of 4), row stride ts elements.  Part m writes
+// columns 2m and 2m + 1.
+__device__ __forceinline__ void store_4x8_transposed_part(bf16_t* lds, int ts, int lr0, int c0,
+                                                          const uint4 (&x)[4], int m) {
+  bf16_t* dst = lds + c0 * ts + tpos(lr0);
+  const uint32_t a0 = u4word(x[0], m), a1 = u4word(x[1], m);
+  const uint32_t a2 = u4word(x[2], m), a3 = u4word(x[3], m);
+  uint2 even, odd;  // columns 2m and 2m + 1 of the four rows
+  even.x = pack_lo(a0, a1);
+  even.y = pack_lo(a2, a3);
+  odd.x = pack_hi(a0, a1);
+  odd.y = pack_hi(a2, a3);
+  *reinterpret_cast<uint2*>(dst + (2 * m) * ts) = even;
+  *reinterpret_cast<uint2*>(dst + (2 * m + 1) * ts) = odd;
+}
 __device__ __forceinline__ void store_4x8_transposed(bf16_t* lds, int ts, int lr0, int c0,
                                                      const uint4 (&x)[4]) {
-  bf16_t* dst = lds + c0 * ts + tpos(lr0);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const uint32_t a0 = u4word(x[0], m), a1 = u4word(x[1], m);
-    const uint32_t a2 = u4word(x[2], m), a3 = u4word(x[3], m);
-    uint2 even, odd;  // columns 2m and 2m + 1 of the four rows
-    even.x = pack_lo(a0, a1);
-    even.y = pack_lo(a2, a3);
-    odd.x = pack_hi(a0, a1);
-    odd.y = pack_hi(a2, a3);
-    *reinterpret_cast<uint2*>(dst + (2 * m) * ts) = even;
-    *reinterpret_cast<uint2*>(dst + (2 * m + 1) * ts) = odd;
-  }
+  for (int m = 0; m < 4; ++m) store_4x8_transposed_part(lds, ts, lr0, c0, x, m);
 }
 
 // ALiBi position bias, in log2 units: the score of (row, key) gets -slope log2(e) |row - key|
