@@ -920,15 +920,13 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
         // S^T = K Q^T and dP^T = V dO^T: keys k0 + [0, 32) x this wave's rows.
         const bf16_t* kp = sK + (32 * kt + l32) * KSTR + 8 * hh;
         const bf16_t* vp = sV + (32 * kt + l32) * KSTR + 8 * hh;
-        // d <= 128: the operands of k-step cc + 1 are read while k-step cc's products issue
-        // (two named buffers, a scheduling barrier per step), as in the key-block kernel.
-        // dP^T - D comes straight out of the products: the accumulator starts at -D.
-        constexpr bool kAhead = D <= 128;
-        constexpr int kRing = 4, kAh = 3;  // d = 256 operand ring (see below)
-        f32x16 s = zero16(), dp;
+        if constexpr (D <= 128) {
+          // The operands of k-step cc + 1 are read while k-step cc's products issue (two
+          // named buffers, a scheduling barrier per step), as in the key-block kernel.
+          // dP^T - D comes straight out of the products: the accumulator starts at -D.
+          f32x16 s = zero16(), dp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dp[r] = ndval;
-        if constexpr (kAhead) {
+          for (int r = 0; r < 16; ++r) dp[r] = ndval;
           bf16x8 ok[2], ov[2];
           ok[0] = lds_read_b128(kp);
           ov[0] = lds_read_b128(vp);
@@ -945,84 +943,119 @@ __global__ __launch_bounds__(QCfg<D>::NT, 1) void bwd_dq_kernel(
             __builtin_amdgcn_sched_barrier(0);
           }
           __builtin_amdgcn_s_setprio(0);
-        } else {
-          // d = 256: the K / V operands stream through rings of kRing registers, read kAh
-          // k-steps ahead, which leaves the Q and dO operands their VGPRs.
-          bf16x8 ok[kRing], ov[kRing];
+          const bf16_t* tp = sKT + l32 * TSTR + 8 * hh + 32 * kt;
+          // K^T operand j = 2 dt + c2 (head-dim tile dt, key half c2)
+          bf16x8 ta[2 * ND];
 #pragma unroll
-          for (int i = 0; i < kAh; ++i) {
-            ok[i] = lds_read_b128(kp + 16 * i);
-            ov[i] = lds_read_b128(vp + 16 * i);
+          for (int j = 0; j < 2 * ND; ++j)
+            ta[j] = lds_read_b128(tp + 32 * (j >> 1) * TSTR + 16 * (j & 1));
+          // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D); masked entries 0.
+          float p[16];
+          {  // position bias: see alibi_addend (key - row of element 0 is k0 + 4 hh - row)
+            const float dbase = AL != 0 ? (float)(k0 + 4 * hh - row) : 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              p[r] = fast_exp2(fmaf(s[r], c, alibi_addend<AL>(slope2, dbase,
+                                                              (float)(8 * (r >> 2) + (r & 3)), lse2)));
           }
+          // Bitwise (branch-free) without a position bias; with one, the short-circuit form,
+          // which here leaves the register allocation without spills.
+          const bool need_mask =
+              AL == 0 ? (k0 + 32 > N) | ((causal != 0) & (k0 + 31 > wr0)) |
+                            ((window > 0) & (k0 < wr0 + 32 - window))
+                      : (k0 + 32 > N) || (causal && k0 + 31 > wr0) ||
+                            (window > 0 && k0 < wr0 + 32 - window);
+          if (need_mask) {
+            const int kb0 = k0 + hh * 4;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int kk = kb0 + (r >> 2) * 8 + (r & 3);
+              p[r] = ((kk >= klo) & (kk <= khi)) ? p[r] : 0.f;
+            }
+          }
+          bf16x8 pS[2];
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const bf16x2 d2 = to_bf16x2(p[r] * dp[r], p[r + 1] * dp[r + 1]);
+            pS[r >> 3][r & 7] = d2[0];
+            pS[r >> 3][(r & 7) + 1] = d2[1];
+          }
+          // dQ^T += K^T dS^T
           __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) {
-            if (cc + kAh < NC) {
-              ok[(cc + kAh) % kRing] = lds_read_b128(kp + 16 * (cc + kAh));
-              ov[(cc + kAh) % kRing] = lds_read_b128(vp + 16 * (cc + kAh));
+          for (int j = 0; j < 2 * ND; ++j) acc[j >> 1] = mfma32(ta[j], pS[j & 1], acc[j >> 1]);
+          __builtin_amdgcn_s_setprio(0);
+        } else {
+          // d = 256 (one wave per SIMD): the S^T products, then the dP^T products with one
+          // weight P^T = exp2(S^T c - LSE log2 e) after each, then the dQ^T products with the
+          // second key half's dS^T between the first half's products.  The K / V / K^T
+          // operands stream through one ring of kRing registers read kAh products ahead,
+          // which leaves the Q and dO operands their VGPRs.  dP^T - D comes straight out of
+          // the products: the accumulator starts at -D.
+          constexpr int kRing = 4, kAh = 3;
+          f32x16 s = zero16(), dp;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[r] = ndval;
+          // position bias: see alibi_addend (key - row of element 0 is k0 + 4 hh - row)
+          const float dbase = AL != 0 ? (float)(k0 + 4 * hh - row) : 0.f;
+          auto opread = [&](int q) { return lds_read_b128((q < NC ? kp : vp) + 16 * (q % NC)); };
+          float p[16];
+          bf16x8 ring[kRing];
+#pragma unroll
+          for (int i = 0; i < kAh; ++i) ring[i] = opread(i);
+#pragma unroll
+          for (int q = 0; q < 2 * NC; ++q) {
+            if (q + kAh < 2 * NC) ring[(q + kAh) % kRing] = opread(q + kAh);
+            if (q < NC) {
+              s = mfma32(ring[q % kRing], qop[q], s);
+            } else {
+              const int r = q - NC;
+              dp = mfma32(ring[q % kRing], oop[r], dp);
+              p[r] = fast_exp2(fmaf(s[r], c, alibi_addend<AL>(slope2, dbase,
+                                                              (float)(8 * (r >> 2) + (r & 3)), lse2)));
             }
-            s = mfma32(ok[cc % kRing], qop[cc], s);
-            dp = mfma32(ov[cc % kRing], oop[cc], dp);
             __builtin_amdgcn_sched_barrier(0);
           }
-          __builtin_amdgcn_s_setprio(0);
-        }
-        const bf16_t* tp = sKT + l32 * TSTR + 8 * hh + 32 * kt;
-        // K^T operand j = 2 dt + c2 (head-dim tile dt, key half c2)
-        auto tread = [&](int j) { return lds_read_b128(tp + 32 * (j >> 1) * TSTR + 16 * (j & 1)); };
-        bf16x8 ta[kAhead ? 2 * ND : kRing];
-        if constexpr (kAhead) {
+          // K^T operand of dQ^T product j: head-dim tile j % ND, key half j / ND
+          const bf16_t* tp = sKT + l32 * TSTR + 8 * hh + 32 * kt;
+          auto tread = [&](int j) {
+            return lds_read_b128(tp + 32 * (j % ND) * TSTR + 16 * (j / ND));
+          };
 #pragma unroll
-          for (int j = 0; j < 2 * ND; ++j) ta[j] = tread(j);
-        } else {
+          for (int i = 0; i < kAh; ++i) ring[i] = tread(i);
+          // masked entries 0 (the branch-free condition without a position bias, the
+          // short-circuit one with it, as above)
+          const bool need_mask =
+              AL == 0 ? (k0 + 32 > N) | ((causal != 0) & (k0 + 31 > wr0)) |
+                            ((window > 0) & (k0 < wr0 + 32 - window))
+                      : (k0 + 32 > N) || (causal && k0 + 31 > wr0) ||
+                            (window > 0 && k0 < wr0 + 32 - window);
+          if (need_mask) {
+            const int kb0 = k0 + hh * 4;
 #pragma unroll
-          for (int i = 0; i < kAh; ++i) ta[i] = tread(i);
-        }
-        // P^T = exp2(S^T c - LSE log2 e); dS^T = P^T (dP^T - D); masked entries 0.
-        float p[16];
-        {  // position bias: see alibi_addend (key - row of element 0 is k0 + 4 hh - row)
-          const float dbase = AL != 0 ? (float)(k0 + 4 * hh - row) : 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            p[r] = fast_exp2(fmaf(s[r], c, alibi_addend<AL>(slope2, dbase,
-                                                            (float)(8 * (r >> 2) + (r & 3)), lse2)));
-        }
-        // Bitwise (branch-free) without a position bias; with one, the short-circuit form,
-        // which here leaves the register allocation without spills.
-        const bool need_mask =
-            AL == 0 ? (k0 + 32 > N) | ((causal != 0) & (k0 + 31 > wr0)) |
-                          ((window > 0) & (k0 < wr0 + 32 - window))
-                    : (k0 + 32 > N) || (causal && k0 + 31 > wr0) ||
-                          (window > 0 && k0 < wr0 + 32 - window);
-        if (need_mask) {
-          const int kb0 = k0 + hh * 4;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = kb0 + (r >> 2) * 8 + (r & 3);
-            p[r] = ((kk >= klo) & (kk <= khi)) ? p[r] : 0.f;
+            for (int r = 0; r < 16; ++r) {
+              const int kk = kb0 + (r >> 2) * 8 + (r & 3);
+              p[r] = ((kk >= klo) & (kk <= khi)) ? p[r] : 0.f;
+            }
           }
-        }
-        bf16x8 pS[2];
+          // dS^T = P^T (dP^T - D) as the bf16 B operand, elements r and r + 1
+          bf16x8 pS[2];
+          auto ds_pair = [&](int r) {
+            const bf16x2 d2 = to_bf16x2(p[r] * dp[r], p[r + 1] * dp[r + 1]);
+            pS[r >> 3][r & 7] = d2[0];
+            pS[r >> 3][(r & 7) + 1] = d2[1];
+          };
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const bf16x2 d2 = to_bf16x2(p[r] * dp[r], p[r + 1] * dp[r + 1]);
-          pS[r >> 3][r & 7] = d2[0];
-          pS[r >> 3][(r & 7) + 1] = d2[1];
-        }
-        // dQ^T += K^T dS^T
-        __builtin_amdgcn_s_setprio(1);
-        if constexpr (kAhead) {
-#pragma unroll
-          for (int j = 0; j < 2 * ND; ++j) acc[j >> 1] = mfma32(ta[j], pS[j & 1], acc[j >> 1]);
-        } else {
+          for (int r = 0; r < 8; r += 2) ds_pair(r);
+          // dQ^T += K^T dS^T
 #pragma unroll
           for (int j = 0; j < 2 * ND; ++j) {
-            if (j + kAh < 2 * ND) ta[(j + kAh) % kRing] = tread(j + kAh);
-            acc[j >> 1] = mfma32(ta[j % kRing], pS[j & 1], acc[j >> 1]);
+            if (j + kAh < 2 * ND) ring[(j + kAh) % kRing] = tread(j + kAh);
+            acc[j % ND] = mfma32(ring[j % kRing], pS[j / ND], acc[j % ND]);
+            if (j < 8 && (j & 1) == 0) ds_pair(8 + j);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
-        __builtin_amdgcn_s_setprio(0);
       }
     }
     if (nb + 1 < nb_hi) {
