@@ -162,7 +162,10 @@ __global__ __launch_bounds__(512) void issue_chain_kernel(float* __restrict__ ou
 // The workgroup uses 64 KiB of LDS; every address stays inside it.
 constexpr int kIssueLdsBytes = 65536;
 
-template <int NR>
+// AGPR = true: the accumulators live in AGPRs (assembly products, as the head-dim-256
+// kernels hold theirs), so the products' accumulator reads and writes stay out of the VGPRs
+// that the LDS reads fill.
+template <int NR, bool AGPR = false>
 __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out, int iters) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -184,6 +187,10 @@ __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out,
   f32x16 acc[kProbeChains];
 #pragma unroll
   for (int j = 0; j < kProbeChains; ++j) acc[j] = zero16();
+  if constexpr (AGPR) {  // wait states between the zeroing writes and the first product
+#pragma unroll
+    for (int j = 0; j < kProbeChains; ++j) asm volatile("s_nop 4" : "+a"(acc[j]));
+  }
   bf16x8 sa[2][kProbeChains], sb[2][kProbeChains];
   auto load = [&](int set, int it) {
 #pragma unroll
@@ -194,8 +201,12 @@ __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out,
   };
   auto products = [&](int set) {
 #pragma unroll
-    for (int j = 0; j < kProbeChains; ++j)
-      acc[j] = mfma32(NR >= 1 ? sa[set][j] : k0, NR >= 2 ? sb[set][j] : k1, acc[j]);
+    for (int j = 0; j < kProbeChains; ++j) {
+      const bf16x8& a = NR >= 1 ? sa[set][j] : k0;
+      const bf16x8& b = NR >= 2 ? sb[set][j] : k1;
+      if constexpr (AGPR) mfma_acc(acc[j], a, b);
+      else acc[j] = mfma32(a, b, acc[j]);
+    }
   };
   load(0, 0);
   for (int it = 0; it < iters; it += 2) {
@@ -207,6 +218,10 @@ __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out,
     __builtin_amdgcn_sched_barrier(0);
     products(1);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (AGPR) {  // the last product's latency before vector reads of the results
+#pragma unroll
+    for (int j = 0; j < kProbeChains; ++j) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(acc[j]));
   }
   float s = 0.f;
 #pragma unroll
@@ -307,6 +322,9 @@ hipError_t launch_issue_probe(float* out, int kind, int param, int waves_per_sim
     case 300: return launch_issue(issue_lds_kernel<0>, blocks, threads, kIssueLdsBytes, out, iters, st);
     case 301: return launch_issue(issue_lds_kernel<1>, blocks, threads, kIssueLdsBytes, out, iters, st);
     case 302: return launch_issue(issue_lds_kernel<2>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    case 310: return launch_issue(issue_lds_kernel<0, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    case 311: return launch_issue(issue_lds_kernel<1, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    case 312: return launch_issue(issue_lds_kernel<2, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
     default: return hipErrorInvalidValue;
   }
 }

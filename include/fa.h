@@ -304,7 +304,9 @@ fa_status fa_atomic_probe(float* acc, int row_blocks, int stride, int blocks, in
  *                               chains (eight products per round for this kind);
  *   3  param in {0,1,2}:        param operands of each product read from LDS (16 bytes per
  *                               lane, one round ahead; 64 KiB of LDS per workgroup; iters
- *                               is rounded up to an even count).
+ *                               is rounded up to an even count); param in {10,11,12}: the
+ *                               same with param - 10 LDS operands and the accumulators
+ *                               held in AGPRs instead of VGPRs.
  *   4, 5  param = width * 10000 + stride, width in {4,8,16} bytes, stride in [1, 4096]:
  *                               no products; every wave stores (4) or loads (5) `width`
  *                               bytes per lane at LDS byte lane * stride (masked to 64 KiB
