@@ -103,6 +103,7 @@ ISSUE_PROBES = {  # kind: (name, params) of fa_issue_probe
     1: ("exp_per_mfma", (1, 2, 3, 4, 6, 8)),
     2: ("chains", (1, 2, 4, 8)),
     3: ("lds_operands_per_mfma", (0, 1, 2, 10, 11, 12)),
+    6: ("global_operand_per_mfma", (1, 2, 3)),
 }
 
 
@@ -110,7 +111,7 @@ def issue_probe(fa, torch, dev, stream, iters: int = 4000, reps: int = 3):
     """Matrix-core throughput (fraction of the 2516.6 TFLOP/s peak, best of reps) with the
     fa_issue_probe variants, one workgroup per CU at one and two waves per SIMD."""
     blocks = 256
-    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    out = torch.zeros(blocks * 512, dtype=torch.float32, device=dev)
     sh = stream.cuda_stream
     res = {}
     for kind, (name, params) in ISSUE_PROBES.items():
@@ -130,7 +131,8 @@ def issue_probe(fa, torch, dev, stream, iters: int = 4000, reps: int = 3):
                     e1.synchronize()
                     ms = e0.elapsed_time(e1)
                     best = ms if best is None else min(best, ms)
-                rounds = iters + (iters & 1) if kind == 3 else iters
+                rounds = (iters + (iters & 1) if kind == 3 else
+                          (iters + 3) // 4 * 4 if kind == 6 else iters)
                 products = 8 if kind == 2 else 4
                 flop = blocks * 4 * wps * rounds * products * 32768.0
                 row[str(param)] = round(flop / (best * 1e-3) / 1e12 / 2516.6, 4)

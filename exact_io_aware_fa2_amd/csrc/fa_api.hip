@@ -338,6 +338,7 @@ static bool issue_probe_supported(int kind, int param) {
     case 1: return param == 1 || param == 2 || param == 3 || param == 4 || param == 6 || param == 8;
     case 2: return param == 1 || param == 2 || param == 4 || param == 8;
     case 3: return param == 0 || param == 1 || param == 2 || param == 10 || param == 11 || param == 12;
+    case 6: return param == 1 || param == 2 || param == 3;
     case 4:
     case 5: {  // LDS bank probe: width * 10000 + stride
       const int width = param / 10000, stride = param % 10000;
@@ -355,6 +356,8 @@ fa_status fa_issue_probe(float* out, int kind, int param, int waves_per_simd, in
   if ((waves_per_simd != 1 && waves_per_simd != 2) || blocks <= 0 || iters <= 0)
     return fail(FA_ERR_INVALID_ARG,
                 "fa_issue_probe: waves_per_simd must be 1 or 2, blocks and iters positive");
+  if (kind == 6 && blocks * waves_per_simd < 32)  // `out` must hold one 32 KiB read window
+    return fail(FA_ERR_INVALID_ARG, "fa_issue_probe: kind 6 needs blocks * waves_per_simd >= 32");
   return launched("fa_issue_probe", fa::launch_issue_probe(out, kind, param, waves_per_simd,
                                                            blocks, iters, (hipStream_t)stream));
 }

@@ -231,6 +231,85 @@ __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out,
   out[blockIdx.x * blockDim.x + t] = s;
 }
 
+// kind 6: the A operand of each product read from global memory with 16-byte buffer loads
+// (the B operand stays in registers), issued kGlbSets - 1 rounds ahead through a ring of
+// register sets, so the load latency is covered as it would be a whole key tile ahead.
+// Each workgroup reads a 32 KiB window of `out` (L1 / L2 resident after the first round):
+//   MODE 1: each wave reads a 1 KiB run (consecutive lanes, consecutive 16 bytes);
+//   MODE 2: the K-operand pattern of the forward kernel: lane (l, h) reads 16 bytes at
+//           row l (256-byte rows of a 32-row, 8 KiB tile), byte 16 h + 32 j in round j;
+//   MODE 3: chains 0-1 as MODE 2, chains 2-3 read their A operand from LDS one round ahead
+//           (half the products with a global operand, half with an LDS one, as a forward
+//           with K from global memory and V^T from LDS would have).
+// The loads go through a buffer resource that ends at the window, so no address leaves it.
+constexpr int kGlbSets = 4;
+constexpr uint32_t kGlbWindow = 32768;
+
+template <int MODE>
+__global__ __launch_bounds__(512) void issue_glb_kernel(float* __restrict__ out, int iters) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, l32 = lane & 31, hh = lane >> 5;
+  if constexpr (MODE == 3) {
+    for (int i = t; i < kIssueLdsBytes / 4; i += blockDim.x)
+      reinterpret_cast<float*>(smem)[i] = 0.001f * (float)(i & 255);
+    __syncthreads();
+  }
+  const uint32_t nwin = (uint32_t)gridDim.x * blockDim.x * 4u / kGlbWindow;  // >= 1 (host)
+  const rsrc_t res =
+      make_rsrc(reinterpret_cast<const char*>(out) + (size_t)(blockIdx.x % nwin) * kGlbWindow,
+                kGlbWindow);
+  auto goff = [&](int it, int c) -> uint32_t {
+    if constexpr (MODE == 1)
+      return (uint32_t)(((w * 1024 + c * 8192 + (it & 3) * 2048) & (int)(kGlbWindow - 1024)) +
+                        lane * 16);
+    return (uint32_t)(((c + 4 * (it & 1) + w) & 3) * 8192 + l32 * 256 + hh * 16 +
+                      ((it >> 1) & 7) * 32);
+  };
+  auto loff = [&](int it, int c) {
+    return ((w * 1024 + c * 8192 + (it & 3) * 2048) & (kIssueLdsBytes - 1024)) + lane * 16;
+  };
+  constexpr int NG = MODE == 3 ? 2 : kProbeChains;  // chains with a global operand
+  bf16x8 k1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) k1[i] = (__bf16)(0.002f * i);
+  f32x16 acc[kProbeChains];
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j) acc[j] = zero16();
+  bf16x8 ga[kGlbSets][NG], la[2][kProbeChains];
+  auto gload = [&](int set, int it) {
+#pragma unroll
+    for (int j = 0; j < NG; ++j) ga[set][j] = __builtin_bit_cast(bf16x8, bload16(res, goff(it, j)));
+  };
+  auto lload = [&](int set, int it) {
+#pragma unroll
+    for (int j = NG; j < kProbeChains; ++j) la[set][j] = lds_read_b128(smem + loff(it, j));
+  };
+  auto products = [&](int gset, int lset) {
+#pragma unroll
+    for (int j = 0; j < kProbeChains; ++j)
+      acc[j] = mfma32(j < NG ? ga[gset][j] : la[lset][j], k1, acc[j]);
+  };
+#pragma unroll
+  for (int s2 = 0; s2 < kGlbSets - 1; ++s2) gload(s2, s2);
+  if constexpr (MODE == 3) lload(0, 0);
+  for (int it = 0; it < iters; it += kGlbSets) {
+#pragma unroll
+    for (int r = 0; r < kGlbSets; ++r) {
+      gload((r + kGlbSets - 1) % kGlbSets, it + r + kGlbSets - 1);
+      if constexpr (MODE == 3) lload((r + 1) & 1, it + r + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      products(r, r & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kProbeChains; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += acc[j][r];
+  out[blockIdx.x * blockDim.x + t] = s;
+}
+
 // LDS bank probe: every wave of the workgroup accesses 64 KiB of LDS at lane * stride
 // bytes (masked to the array and aligned to the access width) `iters` times, with a
 // compiler barrier between rounds so every access is issued; W bytes per access.
@@ -325,6 +404,9 @@ hipError_t launch_issue_probe(float* out, int kind, int param, int waves_per_sim
     case 310: return launch_issue(issue_lds_kernel<0, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
     case 311: return launch_issue(issue_lds_kernel<1, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
     case 312: return launch_issue(issue_lds_kernel<2, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    case 601: return launch_issue(issue_glb_kernel<1>, blocks, threads, 0, out, iters, st);
+    case 602: return launch_issue(issue_glb_kernel<2>, blocks, threads, 0, out, iters, st);
+    case 603: return launch_issue(issue_glb_kernel<3>, blocks, threads, kIssueLdsBytes, out, iters, st);
     default: return hipErrorInvalidValue;
   }
 }

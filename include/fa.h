@@ -307,6 +307,15 @@ fa_status fa_atomic_probe(float* acc, int row_blocks, int stride, int blocks, in
  *                               is rounded up to an even count); param in {10,11,12}: the
  *                               same with param - 10 LDS operands and the accumulators
  *                               held in AGPRs instead of VGPRs.
+ *   6  param in {1,2,3}:        the A operand of each product read from global memory
+ *                               (16-byte loads three rounds ahead, inside a 32 KiB window of
+ *                               `out` per workgroup; `out` is overwritten, its values are
+ *                               the operands): 1 a contiguous 1 KiB run per wave, 2 the
+ *                               K-operand pattern of the forward (32 rows of 256 bytes, 32
+ *                               bytes per row per load), 3 half the products as 2 and half
+ *                               with the A operand from LDS; needs blocks * waves_per_simd
+ *                               >= 32 (FA_ERR_INVALID_ARG otherwise); iters is rounded up
+ *                               to a multiple of 4.
  *   4, 5  param = width * 10000 + stride, width in {4,8,16} bytes, stride in [1, 4096]:
  *                               no products; every wave stores (4) or loads (5) `width`
  *                               bytes per lane at LDS byte lane * stride (masked to 64 KiB

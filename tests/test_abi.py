@@ -132,6 +132,10 @@ def test_issue_probe_validation():
     assert fa.fa_issue_probe(1 << 20, 0, 4, 2, 0, 4, stream=0) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_issue_probe(1 << 20, 0, 4, 2, 4, 0, stream=0) == fa.FA_ERR_INVALID_ARG
     assert fa.fa_last_error().startswith("fa_issue_probe")
+    # global-operand probes read a 32 KiB window of `out` per workgroup
+    assert fa.fa_issue_probe(1 << 20, 6, 4, 2, 256, 4, stream=0) == fa.FA_ERR_UNSUPPORTED
+    assert fa.fa_issue_probe(1 << 20, 6, 2, 1, 31, 4, stream=0) == fa.FA_ERR_INVALID_ARG
+    assert fa.fa_issue_probe(1 << 20, 6, 2, 2, 15, 4, stream=0) == fa.FA_ERR_INVALID_ARG
     # LDS bank probes: width * 10000 + stride, width in {4, 8, 16}, stride in [1, 4096]
     for kind in (4, 5):
         for param in (0, 30128, 40000, 44097, 20008, -40004):
