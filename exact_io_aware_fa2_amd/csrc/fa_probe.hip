@@ -6,8 +6,9 @@
 //     of dQ would have (the alternative to the separate dQ pass of the backward), so the
 //     choice between the two can be priced with a measured atomic rate;
 //   * issue probes: matrix products next to the other work the attention kernels put
-//     beside them (FMAs, exp2, LDS operand reads) and dependent product chains, to measure
-//     how much of that work the matrix core's issue pattern leaves room for.
+//     beside them (FMAs, exp2, LDS operand reads, operands loaded from global memory) and
+//     dependent product chains, to measure how much of that work the matrix core's issue
+//     pattern leaves room for.
 //   * LDS bank probes: every lane of a wave stores to (or loads from) LDS at lane * stride
 //     bytes, so the bank-conflict counters of the launch give the bank count and the lanes
 //     served per cycle for each access width (the layouts of the staged tiles rest on them);
