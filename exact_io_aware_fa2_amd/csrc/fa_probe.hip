@@ -170,8 +170,11 @@ template <int NR, bool AGPR = false>
 __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out, int iters) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  for (int i = t; i < kIssueLdsBytes / 4; i += blockDim.x)
-    reinterpret_cast<float*>(smem)[i] = 0.001f * (float)(i & 255);
+  // bf16 pairs of small values, so the products stay finite and runs can be compared
+  for (int i = t; i < kIssueLdsBytes / 4; i += blockDim.x) {
+    const bf16x2 v = to_bf16x2(0.001f * (float)(i & 255), 0.002f * (float)(i & 127));
+    reinterpret_cast<uint32_t*>(smem)[i] = __builtin_bit_cast(uint32_t, v);
+  }
   __syncthreads();
   // byte offset of operand r of chain c in round it: a 1 KiB-aligned run per wave
   auto off = [&](int it, int c, int r) {
@@ -188,7 +191,11 @@ __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out,
   f32x16 acc[kProbeChains];
 #pragma unroll
   for (int j = 0; j < kProbeChains; ++j) acc[j] = zero16();
-  if constexpr (AGPR) {  // wait states between the zeroing writes and the first product
+  if constexpr (AGPR) {
+    // Wait states between the vector writes of the register operands and of the zeroed
+    // accumulators and the first assembly product (the compiler inserts none for inline
+    // assembly; without them the first product read stale operands).
+    asm volatile("s_nop 4" : "+v"(k0), "+v"(k1));
 #pragma unroll
     for (int j = 0; j < kProbeChains; ++j) asm volatile("s_nop 4" : "+a"(acc[j]));
   }
@@ -251,8 +258,10 @@ __global__ __launch_bounds__(512) void issue_glb_kernel(float* __restrict__ out,
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, l32 = lane & 31, hh = lane >> 5;
   if constexpr (MODE == 3) {
-    for (int i = t; i < kIssueLdsBytes / 4; i += blockDim.x)
-      reinterpret_cast<float*>(smem)[i] = 0.001f * (float)(i & 255);
+    for (int i = t; i < kIssueLdsBytes / 4; i += blockDim.x) {
+      const bf16x2 v = to_bf16x2(0.001f * (float)(i & 255), 0.002f * (float)(i & 127));
+      reinterpret_cast<uint32_t*>(smem)[i] = __builtin_bit_cast(uint32_t, v);
+    }
     __syncthreads();
   }
   const uint32_t nwin = (uint32_t)gridDim.x * blockDim.x * 4u / kGlbWindow;  // >= 1 (host)
