@@ -135,3 +135,32 @@ def test_alibi_bench_workload_sampled():
                                                    slope=sl[h])
         check_grad(dk.float().cpu()[b, cols, h].double().numpy(), dk_ref, f"dK cols [b{b},h{h}]")
         check_grad(dv.float().cpu()[b, cols, h].double().numpy(), dv_ref, f"dV cols [b{b},h{h}]")
+
+
+@pytest.mark.timeout(900)
+def test_alibi_bench_workload_full_tensors():
+    """The ALiBi bench workload (B 2, H 32, N 8192, causal, geometric slopes) over whole
+    tensors: O, LSE, dQ, dK and dV of every head from the oracle with the same slopes."""
+    from tests._parity import check_grad as cg, workers
+    w = ALIBI_WORKLOADS["bf16_b2_h32_n8192_d128_causal_alibi"]
+    q, k, v, do = make_inputs(w, "cuda")
+    slopes = torch.tensor(alibi_slopes(w.Hq), dtype=torch.float32, device="cuda")
+    o, lse = fa.forward(q, k, v, causal=w.causal, scale=w.scale, alibi_slopes=slopes)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, causal=w.causal, scale=w.scale,
+                             alibi_slopes=slopes)
+    torch.cuda.synchronize()
+    sl = slopes.cpu().double().numpy()
+    q64, k64, v64, do64 = to64(q), to64(k), to64(v), to64(do)
+    print(f"{w.name}: oracle forward on {workers()} workers", flush=True)
+    o_ref, lse_ref = oracle.attn_fwd(q64, k64, v64, w.causal, 0, w.scale, workers=workers(),
+                                     alibi_slopes=sl)
+    mx, mean = check_o(to64(o), o_ref)
+    lerr = check_lse(to64(lse), lse_ref)
+    del o_ref, lse_ref
+    print(f"{w.name}: oracle backward", flush=True)
+    dq_r, dk_r, dv_r, _ = oracle.attn_bwd(q64, k64, v64, do64, w.causal, 0, w.scale,
+                                          workers=workers(), alibi_slopes=sl)
+    errs = {n: cg(to64(x), r, n) for n, x, r in (("dQ", dq, dq_r), ("dK", dk, dk_r),
+                                                 ("dV", dv, dv_r))}
+    print(f"{w.name}: O max {mx:.3e} mean {mean:.3e}, LSE max {lerr:.3e}, "
+          + ", ".join(f"{n} rel {e:.3e}" for n, e in errs.items()), flush=True)

@@ -2,8 +2,9 @@
 
 Small batches are compared over whole tensors with the float64 oracle's packed-sequence
 functions; the batches mix empty, one-row, ragged and multi-tile sequences under every mask.
-The packed 16384-row workload the bench times is checked on sampled rows and columns of
-each sequence, plus per-sequence properties that hold at any size.
+The packed 16384-row workload the bench times is compared over whole tensors, and on
+sampled rows and columns of each sequence together with per-sequence properties that hold at
+any size.
 """
 
 import numpy as np
@@ -150,3 +151,42 @@ def test_varlen_packed_workload_sampled():
         assert err <= 3e-2 * ref_dv.abs().max().item() + 0.5, (s, err)
     for t in (o_c, lse_c, dq_c, dk_c, dv_c):
         assert torch.isfinite(t).all()
+
+
+def _seq_head_task(args):
+    """Forward and backward of one (sequence, head) pair with the float64 oracle."""
+    q, k, v, do, causal, window, scale = args
+    o, lse = oracle.attn_fwd_head(q, k, v, causal, window, scale)
+    dq, dk, dv, _ = oracle.attn_bwd_head(q, k, v, do, causal, window, scale)
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.timeout(900)
+def test_varlen_packed_workload_full_tensors():
+    """The packed 16384-row bench workload over whole tensors: every (sequence, head) pair's
+    O, LSE, dQ and its share of dK / dV from the oracle, at the bf16 tolerances."""
+    from tests._parity import pool_map, workers
+    w = VARLEN_WORKLOADS["bf16_varlen_t16384_h32_d128_causal"]
+    (q, k, v, do), (o, lse, dq, dk, dv, _) = _run(w)
+    g = w.Hq // w.Hkv
+    q64, k64, v64, do64 = to64(q), to64(k), to64(v), to64(do)
+    cu = w.cu_seqlens
+    pairs = [(s, h) for s in range(len(w.lengths)) for h in range(w.Hq) if w.lengths[s] > 0]
+    print(f"{w.name}: oracle over {len(pairs)} (sequence, head) pairs on {workers()} workers",
+          flush=True)
+    res = pool_map(_seq_head_task, [
+        (q64[cu[s]:cu[s + 1], h], k64[cu[s]:cu[s + 1], h // g], v64[cu[s]:cu[s + 1], h // g],
+         do64[cu[s]:cu[s + 1], h], w.causal, w.window, w.scale) for s, h in pairs])
+    o_ref, lse_ref = np.zeros_like(q64), np.zeros((w.Hq, w.total))
+    dq_ref, dk_ref, dv_ref = np.zeros_like(q64), np.zeros_like(k64), np.zeros_like(v64)
+    for (s, h), (oh, lh, dqh, dkh, dvh) in zip(pairs, res):
+        a, b = cu[s], cu[s + 1]
+        o_ref[a:b, h], lse_ref[h, a:b], dq_ref[a:b, h] = oh, lh, dqh
+        dk_ref[a:b, h // g] += dkh
+        dv_ref[a:b, h // g] += dvh
+    mx, mean = check_o(to64(o), o_ref)
+    lerr = check_lse(to64(lse), lse_ref)
+    errs = {n: check_grad(to64(x), r, n) for n, x, r in (("dQ", dq, dq_ref), ("dK", dk, dk_ref),
+                                                          ("dV", dv, dv_ref))}
+    print(f"{w.name}: O max {mx:.3e} mean {mean:.3e}, LSE max {lerr:.3e}, "
+          + ", ".join(f"{n} rel {e:.3e}" for n, e in errs.items()), flush=True)
