@@ -6,7 +6,8 @@ the second product, so random inputs are checked against the per-row bounds deri
 tests/_parity.py (fp8_score_error, fp8_o_bound, check_fp8_lse).
 Inputs whose scores are small integers with a unit log2 scale make every weight an exact
 power of two: there the rounding is exact and O must meet the bf16 tolerances too, which
-checks tiling, masks and normalisation tightly.
+checks tiling, masks and normalisation tightly.  The 8-bit bench workload is checked over
+whole tensors against the same per-row bounds.
 """
 
 import math
@@ -161,3 +162,41 @@ def test_fp8_bench_workload_sampled():
         check_fp8_o(o_c[b, rows, h].double().numpy(), o_ref, fp8_o_bound(p, vd, o_ref, delta),
                     f"O[b{b},h{h}]")
         check_fp8_lse(lse_c[b, h, rows].double().numpy(), lse_ref, delta)
+
+
+def _fp8_head_task(args):
+    """Worst error / bound ratios (O, LSE) of one head of the fp8 forward against the float64
+    oracle of the dequantised inputs, every row, in chunks of rows."""
+    qd, kd, vd, o, lse, causal, window, scale, fq, fk = args
+    worst_o = worst_l = 0.0
+    for r0 in range(0, qd.shape[0], 512):
+        rows = np.arange(r0, min(r0 + 512, qd.shape[0]))
+        o_ref, lse_ref = oracle.attn_fwd_rows(qd, kd, vd, rows, causal, window, scale)
+        p = oracle.attention_probs_rows(qd, kd, rows, causal, window, scale)
+        delta = fp8_score_error(qd[rows], kd, scale, fq, fk)
+        worst_o = max(worst_o, check_fp8_o(o[rows], o_ref, fp8_o_bound(p, vd, o_ref, delta)))
+        worst_l = max(worst_l, check_fp8_lse(lse[rows], lse_ref, delta))
+    return worst_o, worst_l
+
+
+@pytest.mark.timeout(900)
+def test_fp8_bench_workload_full_tensors():
+    """The 8-bit bench workload over whole tensors: every row of every head within the
+    per-element bounds of the derived fp8 tolerance."""
+    from tests._parity import pool_map, workers
+    w = FP8_WORKLOADS["fp8_b2_h32_n8192_d128_causal"]
+    q8, k8, v8, factors = make_fp8_inputs(w, "cuda")
+    o, lse = fa.forward_fp8(q8, k8, v8, *factors, causal=w.causal, window=w.window,
+                            scale=w.scale)
+    torch.cuda.synchronize()
+    o_c, lse_c = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    g = w.Hq // w.Hkv
+    qc, kc, vc = _codes(q8), _codes(k8), _codes(v8)
+    tasks = [(oracle.dequantize(qc[b, :, h], factors[0]), oracle.dequantize(kc[b, :, h // g], factors[1]),
+              oracle.dequantize(vc[b, :, h // g], factors[2]), o_c[b, :, h], lse_c[b, h], w.causal,
+              w.window, w.scale, float(factors[0]), float(factors[1]))
+             for b in range(w.B) for h in range(w.Hq)]
+    print(f"{w.name}: oracle and bounds over {len(tasks)} heads on {workers()} workers", flush=True)
+    res = pool_map(_fp8_head_task, tasks)
+    print(f"{w.name}: worst O error / bound {max(r[0] for r in res):.3f}, "
+          f"worst LSE error / bound {max(r[1] for r in res):.3f}", flush=True)
