@@ -102,7 +102,7 @@ ISSUE_PROBES = {  # kind: (name, params) of fa_issue_probe
     0: ("fma_per_mfma", (0, 2, 4, 6, 8, 12)),
     1: ("exp_per_mfma", (1, 2, 3, 4, 6, 8)),
     2: ("chains", (1, 2, 4, 8)),
-    3: ("lds_operands_per_mfma", (0, 1, 2, 10, 11, 12)),
+    3: ("lds_operands_per_mfma", (0, 1, 2, 10, 11, 12, 20, 21, 22)),
     6: ("global_operand_per_mfma", (1, 2, 3)),
 }
 

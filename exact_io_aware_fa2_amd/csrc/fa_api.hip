@@ -337,7 +337,8 @@ static bool issue_probe_supported(int kind, int param) {
     case 0: return param == 0 || param == 2 || param == 4 || param == 6 || param == 8 || param == 12;
     case 1: return param == 1 || param == 2 || param == 3 || param == 4 || param == 6 || param == 8;
     case 2: return param == 1 || param == 2 || param == 4 || param == 8;
-    case 3: return param == 0 || param == 1 || param == 2 || param == 10 || param == 11 || param == 12;
+    case 3: return (param >= 0 && param <= 2) || (param >= 10 && param <= 12) ||
+                   (param >= 20 && param <= 22);
     case 6: return param == 1 || param == 2 || param == 3;
     case 4:
     case 5: {  // LDS bank probe: width * 10000 + stride

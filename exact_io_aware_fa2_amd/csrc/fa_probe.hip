@@ -165,14 +165,26 @@ constexpr int kIssueLdsBytes = 65536;
 
 // AGPR = true: the accumulators live in AGPRs (assembly products, as the head-dim-256
 // kernels hold theirs), so the products' accumulator reads and writes stay out of the VGPRs
-// that the LDS reads fill.
-template <int NR, bool AGPR = false>
+// that the LDS reads fill.  RND = true: every operand value (LDS and registers) is drawn
+// uniformly from [-2, 2) by a hash of its position, as attention data varies from element
+// to element, where the other variants use slowly varying small values.
+__device__ __forceinline__ float probe_rnd(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return (float)(x >> 8) * (4.f / 16777216.f) - 2.f;
+}
+
+template <int NR, bool AGPR = false, bool RND = false>
 __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out, int iters) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   // bf16 pairs of small values, so the products stay finite and runs can be compared
   for (int i = t; i < kIssueLdsBytes / 4; i += blockDim.x) {
-    const bf16x2 v = to_bf16x2(0.001f * (float)(i & 255), 0.002f * (float)(i & 127));
+    const bf16x2 v = RND ? to_bf16x2(probe_rnd(2u * i), probe_rnd(2u * i + 1u))
+                         : to_bf16x2(0.001f * (float)(i & 255), 0.002f * (float)(i & 127));
     reinterpret_cast<uint32_t*>(smem)[i] = __builtin_bit_cast(uint32_t, v);
   }
   __syncthreads();
@@ -185,8 +197,9 @@ __global__ __launch_bounds__(512) void issue_lds_kernel(float* __restrict__ out,
   bf16x8 k0, k1;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    k0[i] = (__bf16)(0.001f * (int)(t + i));
-    k1[i] = (__bf16)(0.002f * i);
+    const uint32_t id = (uint32_t)(blockIdx.x * blockDim.x + t) * 16u + (uint32_t)i;
+    k0[i] = (__bf16)(RND ? probe_rnd(0x40000000u + id) : 0.001f * (int)(t + i));
+    k1[i] = (__bf16)(RND ? probe_rnd(0x80000000u + id) : 0.002f * i);
   }
   f32x16 acc[kProbeChains];
 #pragma unroll
@@ -414,6 +427,9 @@ hipError_t launch_issue_probe(float* out, int kind, int param, int waves_per_sim
     case 310: return launch_issue(issue_lds_kernel<0, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
     case 311: return launch_issue(issue_lds_kernel<1, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
     case 312: return launch_issue(issue_lds_kernel<2, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    case 320: return launch_issue(issue_lds_kernel<0, false, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    case 321: return launch_issue(issue_lds_kernel<1, false, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
+    case 322: return launch_issue(issue_lds_kernel<2, false, true>, blocks, threads, kIssueLdsBytes, out, iters, st);
     case 601: return launch_issue(issue_glb_kernel<1>, blocks, threads, 0, out, iters, st);
     case 602: return launch_issue(issue_glb_kernel<2>, blocks, threads, 0, out, iters, st);
     case 603: return launch_issue(issue_glb_kernel<3>, blocks, threads, kIssueLdsBytes, out, iters, st);

@@ -306,7 +306,9 @@ fa_status fa_atomic_probe(float* acc, int row_blocks, int stride, int blocks, in
  *                               lane, one round ahead; 64 KiB of LDS per workgroup; iters
  *                               is rounded up to an even count); param in {10,11,12}: the
  *                               same with param - 10 LDS operands and the accumulators
- *                               held in AGPRs instead of VGPRs.
+ *                               held in AGPRs instead of VGPRs; param in {20,21,22}:
+ *                               param - 20 LDS operands, every operand value drawn
+ *                               uniformly from [-2, 2) (element-to-element variation).
  *   6  param in {1,2,3}:        the A operand of each product read from global memory
  *                               (16-byte loads three rounds ahead, inside a 32 KiB window of
  *                               `out` per workgroup; `out` is overwritten, its values are

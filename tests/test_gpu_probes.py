@@ -59,7 +59,8 @@ def test_issue_probe_agpr_accumulators_match_vgpr(nr):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("kind,param", [(0, 4), (1, 2), (2, 1), (6, 1), (6, 2), (6, 3)])
+@pytest.mark.parametrize("kind,param", [(0, 4), (1, 2), (2, 1), (3, 20), (3, 22), (6, 1), (6, 2),
+                                        (6, 3)])
 def test_issue_probe_kinds_complete(kind, param):
     blocks, wps, iters = 32, 1, 40
     out = torch.zeros(blocks * 256 * wps, device="cuda", dtype=torch.float32)
